@@ -1,0 +1,183 @@
+/*
+ * fg8.h - fine-grained-scaled FP8 GEMM on AMD MI355X (gfx950): the C ABI of
+ * libfg8.so.
+ *
+ * The method (DeepSeek's DeepGEMM as described by the pages this library is
+ * built from): FP32 tensors are multiplied by per-group scaling factors and
+ * converted to FP8, the GEMM runs on FP8 inputs, and the result is restored to
+ * FP32 (cuda-deepseek blog, hrletsgo.me, list item 5 of the custom
+ * mixed-precision loop); the FP8 partial sums of the matrix units are promoted
+ * at a fixed interval into FP32 accumulators where the scales are applied
+ * (DeepGEMM release news, ctol-kr.com, section 1 "FP8": two-level
+ * accumulation); besides the dense GEMM there are MoE grouped GEMMs in a
+ * contiguous and a masked layout (same article, section 4 "MoE"; DeepGEMM
+ * explainer, opsoai.com, MoE section); MXFP8 shares one power-of-two exponent
+ * per 32 elements (aitrends.kr article on DeepSeek-V3 MoE training on B200,
+ * MXFP8 section and glossary).
+ *
+ * Formats fixed here (the pages name only "FP8"):
+ *   e4m3     OCP FP8 E4M3, no infinities, NaN = 0x7F/0xFF, max 448; stored as
+ *            uint8.  Encoding rounds to nearest even, saturates at +-448 and
+ *            keeps the sign of zero.
+ *   1x128    one FP32 scale per row per 128 consecutive K elements,
+ *            s = fl32(amax / 448) (s = 1 for an all-zero group),
+ *            q = e4m3(fl32(x / s)).
+ *   128x128  one FP32 scale per 128x128 block, same rule; a block cut by the
+ *            end of the rows takes its amax over the rows that exist.
+ *   MX 1x32  one E8M0 byte per row per 32 consecutive K elements:
+ *            E = clamp(floor(log2 amax) - 8, -127, 127), byte = E + 127
+ *            (0 for an all-zero block), q = e4m3(x * 2^-E), value 2^(byte-127).
+ * A dequantized element is e4m3(q) * scale.  Every GEMM computes
+ *   D[m][n] = sum_k A[m][k] * B[n][k]
+ * with A [rows][K] and B [N][K] both K-contiguous (B is a Linear weight
+ * [out][in]), accumulating in FP32 and storing FP32 or BF16 (round to
+ * nearest even).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE memory owned by the caller and must be 16-byte
+ *     aligned.  The library allocates nothing, keeps no state between calls,
+ *     never synchronizes and never exits the process; work is queued on
+ *     `stream` (NULL = the default stream) and the call returns at once.
+ *   - Returns FG8_OK, or FG8_EINVAL (NULL or misaligned pointer, a size out
+ *     of range), FG8_EUNSUPPORTED (a shape this library does not handle), or
+ *     FG8_EHIP (the kernel launch failed).  On FG8_EINVAL and
+ *     FG8_EUNSUPPORTED nothing was launched.  fg8_last_error() gives the text
+ *     for the calling thread's last failure.  Faults inside a kernel surface
+ *     at the caller's next synchronization.
+ *   - Device-side index data (block_expert, valid_rows) is trusted: values out
+ *     of range are undefined behaviour.
+ *   - Calls may run concurrently on different streams; a split-K workspace
+ *     must not be shared by calls that can overlap.
+ *   - FP32 inputs to fp8_quantize must be finite.
+ */
+#ifndef FG8_H
+#define FG8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FG8_OK = 0,
+  FG8_EINVAL = 1,
+  FG8_EUNSUPPORTED = 2,
+  FG8_EHIP = 3
+} fg8_status;
+
+typedef enum { FG8_OUT_F32 = 0, FG8_OUT_BF16 = 1 } fg8_out;
+
+typedef enum {
+  FG8_SCALE_1x128 = 0,
+  FG8_SCALE_128x128 = 1,
+  FG8_SCALE_MX1x32 = 2
+} fg8_scale_kind;
+
+/*
+ * fp8_quantize: FP32 -> e4m3 with fine-grained scales (the "multiply by a
+ * scaling factor and convert to FP8" step of the cuda-deepseek blog's
+ * mixed-precision loop, list item 5, at per-group granularity; MX variant per
+ * the aitrends.kr MXFP8 glossary entry).
+ *   x       const float [batch][rows][cols], row-major.
+ *   q       uint8 [batch][rows][cols] e4m3 codes (output).
+ *   scales  output, layout by kind:
+ *             FG8_SCALE_1x128   float   [batch][cols/128][rows]  (K-block major)
+ *             FG8_SCALE_128x128 float   [batch][ceil(rows/128)][cols/128]
+ *             FG8_SCALE_MX1x32  uint8_t [batch][rows][cols/32]   (E8M0 bytes)
+ *   batch >= 1, rows >= 1; cols % 128 == 0 (cols % 32 == 0 for MX), else
+ *   FG8_EUNSUPPORTED.  Results are bit-exact with the formats above.
+ */
+fg8_status fp8_quantize(const float* x, int64_t batch, int64_t rows, int64_t cols,
+                        fg8_scale_kind kind, uint8_t* q, void* scales, hipStream_t stream);
+
+/*
+ * gemm_fp8_blockscaled: dense D = A B^T with 1x128 scales on A and 128x128
+ * scales on B, two-level accumulation (DeepGEMM release news, ctol-kr.com,
+ * section 1; shapes of the DeepGEMM explainer's speed-up table, opsoai.com).
+ *   a  uint8 [m][k]               sa float [k/128][m]
+ *   b  uint8 [n][k]               sb float [ceil(n/128)][k/128]
+ *   d  [m][n] float (FG8_OUT_F32) or bfloat16 bits (FG8_OUT_BF16), row-major.
+ *   m, n >= 1; k % 128 == 0 and k >= 128 (else FG8_EUNSUPPORTED).
+ *   workspace: device memory of at least fg8_gemm_workspace_bytes(m, n, k)
+ *   bytes (NULL allowed when that is 0).  Its first 4096 bytes are per-tile
+ *   arrival counters, the rest FP32 split-K partial sums.  It must be
+ *   zero-filled before its first use; every completed call leaves the
+ *   counters at zero again, so one workspace serves any sequence of shapes
+ *   (of calls that do not overlap).  Too small a workspace is FG8_EINVAL.
+ */
+fg8_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
+                                const float* sb, void* d, fg8_out out, int64_t m, int64_t n,
+                                int64_t k, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* Workspace bytes gemm_fp8_blockscaled needs for this shape (0 if none). */
+size_t fg8_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/*
+ * grouped_gemm_fp8_contiguous: MoE grouped GEMM, contiguous layout (DeepGEMM
+ * release news, ctol-kr.com, section 4; DeepGEMM explainer, MoE section).  The
+ * rows routed to each expert are stacked, each expert's run padded to a
+ * multiple of 128 rows; block_expert names the expert of every 128-row block.
+ *   a  uint8 [m_total][k]         sa float [k/128][m_total]
+ *   b  uint8 [E][n][k]            sb float [E][ceil(n/128)][k/128]
+ *   block_expert int32 [m_total/128], values in [0, E)  (device memory)
+ *   d  [m_total][n] float or bfloat16 bits.  Every row is written, padding
+ *   rows included (they are zero when the padding rows of a are zero).
+ *   m_total % 128 == 0, k % 128 == 0 (else FG8_EUNSUPPORTED); E = num_experts >= 1.
+ */
+fg8_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const uint8_t* b,
+                                       const float* sb, const int32_t* block_expert, void* d,
+                                       fg8_out out, int64_t m_total, int64_t n, int64_t k,
+                                       int32_t num_experts, hipStream_t stream);
+
+/*
+ * grouped_gemm_fp8_masked: MoE grouped GEMM, masked layout (DeepGEMM release
+ * news, ctol-kr.com, section 4: expert activation may be sparse).  Each expert
+ * owns a fixed block of cap rows of which only the first valid_rows[e] are
+ * live; the counts stay in device memory (no host synchronization, so the
+ * call can be captured in a graph).
+ *   a  uint8 [E][cap][k]          sa float [E][k/128][cap]
+ *   b  uint8 [E][n][k]            sb float [E][ceil(n/128)][k/128]
+ *   valid_rows int32 [E], values in [0, cap]  (device memory)
+ *   d  [E][cap][n]: rows r < valid_rows[e] are written; rows at or past the
+ *   count are never written (and rows of a and sa there are never read).
+ *   cap >= 1, k % 128 == 0 (else FG8_EUNSUPPORTED); E = num_experts >= 1.
+ */
+fg8_status grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uint8_t* b,
+                                   const float* sb, const int32_t* valid_rows, void* d,
+                                   fg8_out out, int32_t num_experts, int64_t cap, int64_t n,
+                                   int64_t k, hipStream_t stream);
+
+/*
+ * gemm_mxfp8: MXFP8 grouped GEMM (aitrends.kr article, MXFP8 section: MXFP8
+ * grouped GEMM for the MoE experts; glossary: one shared exponent per 32
+ * elements).  The E8M0 scales are applied by the gfx950 scaled MFMA, so there
+ * is no separate promotion step.
+ *   a  uint8 [G][m][k]            sa_e8m0 uint8 [G][m][k/32]
+ *   b  uint8 [G][n][k]            sb_e8m0 uint8 [G][n][k/32]
+ *   valid_rows NULL (every row of every group) or int32 [G] in [0, m]
+ *   (device memory; masked layout as in grouped_gemm_fp8_masked)
+ *   d  [G][m][n] float or bfloat16 bits.
+ *   k % 128 == 0 (else FG8_EUNSUPPORTED); G = num_groups >= 1, m, n >= 1.
+ *   E8M0 byte 0xFF (NaN) is not a valid input.
+ */
+fg8_status gemm_mxfp8(const uint8_t* a, const uint8_t* sa_e8m0, const uint8_t* b,
+                      const uint8_t* sb_e8m0, const int32_t* valid_rows, void* d, fg8_out out,
+                      int32_t num_groups, int64_t m_per_group, int64_t n, int64_t k,
+                      hipStream_t stream);
+
+/* Text of the calling thread's last non-OK status ("" if none). */
+const char* fg8_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fg8_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FG8_H */

@@ -1,1 +1,16 @@
-"""Fine-grained-scaled FP8 GEMM for MI355X (gfx950)."""
+"""Fine-grained-scaled FP8 GEMM for MI355X (gfx950).
+
+The entry points mirror the C ABI of libfg8.so (include/fg8.h).  Importing
+the package does not load the library; the first call does, and raises if it
+has not been built.
+"""
+from ._lib import (  # noqa: F401
+    Fg8Error,
+    fp8_quantize,
+    gemm_fp8_blockscaled,
+    gemm_mxfp8,
+    gemm_workspace_bytes,
+    grouped_gemm_fp8_contiguous,
+    grouped_gemm_fp8_masked,
+    version,
+)

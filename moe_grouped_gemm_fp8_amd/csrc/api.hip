@@ -1,0 +1,202 @@
+// C ABI of libfg8.so: argument checks, tile selection and launches.
+// Every entry point validates before it launches anything; see fg8.h for the
+// meaning, layout and ownership of each argument.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "fg8.h"
+#include "fg8_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fg8_status fail(fg8_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define FG8_CHECK_PTR(p)                                                                  \
+  do {                                                                                    \
+    if (!(p)) return fail(FG8_EINVAL, "%s: %s is NULL", fn, #p);                          \
+    if (!aligned16(p)) return fail(FG8_EINVAL, "%s: %s is not 16-byte aligned", fn, #p);  \
+  } while (0)
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;   // row / column counts must fit int32
+constexpr int64_t kMaxK = 16384;                // sb staging covers 128 K blocks per unit
+
+fg8_status check_k(const char* fn, int64_t k) {
+  if (k < 128 || k > kMaxK) return fail(FG8_EUNSUPPORTED, "%s: k=%lld must be in [128, %lld]", fn,
+                                        (long long)k, (long long)kMaxK);
+  if (k % 128) return fail(FG8_EUNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
+  return FG8_OK;
+}
+
+fg8_status run(fg8::GemmProblem& p, const char* fn, hipStream_t stream) {
+  const fg8::TileChoice t = fg8::choose_tiles(p, fg8::device_cu_count());
+  const hipError_t e = fg8::launch_gemm(p, t, stream);
+  if (e != hipSuccess) return fail(FG8_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  g_err[0] = 0;
+  return FG8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fg8_version(void) { return 100; }   // 0.1.0
+
+const char* fg8_last_error(void) { return g_err; }
+
+fg8_status fp8_quantize(const float* x, int64_t batch, int64_t rows, int64_t cols,
+                        fg8_scale_kind kind, uint8_t* q, void* scales, hipStream_t stream) {
+  const char* fn = "fp8_quantize";
+  FG8_CHECK_PTR(x);
+  FG8_CHECK_PTR(q);
+  FG8_CHECK_PTR(scales);
+  if (batch < 1 || rows < 1 || cols < 1 || batch >= 65536 || rows >= kMaxDim || cols >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: bad sizes batch=%lld rows=%lld cols=%lld", fn, (long long)batch,
+                (long long)rows, (long long)cols);
+  if (kind != FG8_SCALE_1x128 && kind != FG8_SCALE_128x128 && kind != FG8_SCALE_MX1x32)
+    return fail(FG8_EINVAL, "%s: unknown scale kind %d", fn, (int)kind);
+  const int64_t unit = kind == FG8_SCALE_MX1x32 ? 32 : 128;
+  if (cols % unit)
+    return fail(FG8_EUNSUPPORTED, "%s: cols=%lld is not a multiple of %lld", fn, (long long)cols,
+                (long long)unit);
+  if (kind == FG8_SCALE_128x128 && (rows + 127) / 128 >= 65536)
+    return fail(FG8_EUNSUPPORTED, "%s: too many row blocks", fn);
+  if (kind != FG8_SCALE_MX1x32 && cols / 128 >= 65536)
+    return fail(FG8_EUNSUPPORTED, "%s: too many column blocks", fn);
+  const hipError_t e = fg8::launch_quantize(x, batch, rows, cols, (int)kind, q, scales, stream);
+  if (e != hipSuccess) return fail(FG8_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  g_err[0] = 0;
+  return FG8_OK;
+}
+
+size_t fg8_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 1 || n < 1 || k < 128 || k % 128 || k > kMaxK) return 0;
+  return fg8::splitk_workspace_bytes(m, n, k, fg8::device_cu_count());
+}
+
+fg8_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t* b,
+                                const float* sb, void* d, fg8_out out, int64_t m, int64_t n,
+                                int64_t k, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  const char* fn = "gemm_fp8_blockscaled";
+  FG8_CHECK_PTR(a);
+  FG8_CHECK_PTR(sa);
+  FG8_CHECK_PTR(b);
+  FG8_CHECK_PTR(sb);
+  FG8_CHECK_PTR(d);
+  if (out != FG8_OUT_F32 && out != FG8_OUT_BF16) return fail(FG8_EINVAL, "%s: bad out", fn);
+  if (m < 1 || n < 1 || m >= kMaxDim || n >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: bad sizes m=%lld n=%lld", fn, (long long)m, (long long)n);
+  if (fg8_status s = check_k(fn, k)) return s;
+  fg8::GemmProblem p{};
+  p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.d = d;
+  p.out_bf16 = out == FG8_OUT_BF16;
+  p.mode = fg8::kDense; p.M = m; p.N = n; p.K = k; p.groups = 1;
+  const fg8::TileChoice t = fg8::choose_tiles(p, fg8::device_cu_count());
+  if (t.splits > 1) {
+    const size_t need = fg8::splitk_workspace_bytes(m, n, k, fg8::device_cu_count());
+    if (!workspace || workspace_bytes < need)
+      return fail(FG8_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(FG8_EINVAL, "%s: workspace misaligned", fn);
+    p.ws_counters = (int32_t*)workspace;
+    p.ws_partial = (float*)((char*)workspace + fg8::kSplitKCounterBytes);
+  }
+  const hipError_t e = fg8::launch_gemm(p, t, stream);
+  if (e != hipSuccess) return fail(FG8_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  g_err[0] = 0;
+  return FG8_OK;
+}
+
+fg8_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const uint8_t* b,
+                                       const float* sb, const int32_t* block_expert, void* d,
+                                       fg8_out out, int64_t m_total, int64_t n, int64_t k,
+                                       int32_t num_experts, hipStream_t stream) {
+  const char* fn = "grouped_gemm_fp8_contiguous";
+  FG8_CHECK_PTR(a);
+  FG8_CHECK_PTR(sa);
+  FG8_CHECK_PTR(b);
+  FG8_CHECK_PTR(sb);
+  FG8_CHECK_PTR(block_expert);
+  FG8_CHECK_PTR(d);
+  if (out != FG8_OUT_F32 && out != FG8_OUT_BF16) return fail(FG8_EINVAL, "%s: bad out", fn);
+  if (num_experts < 1) return fail(FG8_EINVAL, "%s: num_experts=%d", fn, (int)num_experts);
+  if (m_total < 1 || n < 1 || m_total >= kMaxDim || n >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: bad sizes m_total=%lld n=%lld", fn, (long long)m_total,
+                (long long)n);
+  if (m_total % 128)
+    return fail(FG8_EUNSUPPORTED, "%s: m_total=%lld is not a multiple of 128", fn,
+                (long long)m_total);
+  if (fg8_status s = check_k(fn, k)) return s;
+  fg8::GemmProblem p{};
+  p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.d = d;
+  p.out_bf16 = out == FG8_OUT_BF16;
+  p.mode = fg8::kContiguous; p.M = m_total; p.N = n; p.K = k; p.groups = num_experts;
+  p.block_expert = block_expert;
+  return run(p, fn, stream);
+}
+
+fg8_status grouped_gemm_fp8_masked(const uint8_t* a, const float* sa, const uint8_t* b,
+                                   const float* sb, const int32_t* valid_rows, void* d,
+                                   fg8_out out, int32_t num_experts, int64_t cap, int64_t n,
+                                   int64_t k, hipStream_t stream) {
+  const char* fn = "grouped_gemm_fp8_masked";
+  FG8_CHECK_PTR(a);
+  FG8_CHECK_PTR(sa);
+  FG8_CHECK_PTR(b);
+  FG8_CHECK_PTR(sb);
+  FG8_CHECK_PTR(valid_rows);
+  FG8_CHECK_PTR(d);
+  if (out != FG8_OUT_F32 && out != FG8_OUT_BF16) return fail(FG8_EINVAL, "%s: bad out", fn);
+  if (num_experts < 1 || num_experts > 1024)
+    return fail(FG8_EINVAL, "%s: num_experts=%d must be in [1, 1024]", fn, (int)num_experts);
+  if (cap < 1 || n < 1 || cap >= kMaxDim || n >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: bad sizes cap=%lld n=%lld", fn, (long long)cap, (long long)n);
+  if (fg8_status s = check_k(fn, k)) return s;
+  fg8::GemmProblem p{};
+  p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.d = d;
+  p.out_bf16 = out == FG8_OUT_BF16;
+  p.mode = fg8::kMasked; p.M = cap; p.N = n; p.K = k; p.groups = num_experts;
+  p.valid = valid_rows;
+  return run(p, fn, stream);
+}
+
+fg8_status gemm_mxfp8(const uint8_t* a, const uint8_t* sa_e8m0, const uint8_t* b,
+                      const uint8_t* sb_e8m0, const int32_t* valid_rows, void* d, fg8_out out,
+                      int32_t num_groups, int64_t m_per_group, int64_t n, int64_t k,
+                      hipStream_t stream) {
+  const char* fn = "gemm_mxfp8";
+  FG8_CHECK_PTR(a);
+  FG8_CHECK_PTR(sa_e8m0);
+  FG8_CHECK_PTR(b);
+  FG8_CHECK_PTR(sb_e8m0);
+  FG8_CHECK_PTR(d);
+  if (valid_rows && !aligned16(valid_rows))
+    return fail(FG8_EINVAL, "%s: valid_rows is not 16-byte aligned", fn);
+  if (out != FG8_OUT_F32 && out != FG8_OUT_BF16) return fail(FG8_EINVAL, "%s: bad out", fn);
+  if (num_groups < 1 || num_groups > 1024)
+    return fail(FG8_EINVAL, "%s: num_groups=%d must be in [1, 1024]", fn, (int)num_groups);
+  if (m_per_group < 1 || n < 1 || m_per_group >= kMaxDim || n >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: bad sizes m=%lld n=%lld", fn, (long long)m_per_group,
+                (long long)n);
+  if (fg8_status s = check_k(fn, k)) return s;
+  fg8::GemmProblem p{};
+  p.a = a; p.sa = sa_e8m0; p.b = b; p.sb = sb_e8m0; p.d = d;
+  p.out_bf16 = out == FG8_OUT_BF16;
+  p.mx = 1;
+  p.mode = fg8::kMasked; p.M = m_per_group; p.N = n; p.K = k; p.groups = num_groups;
+  p.valid = valid_rows;
+  return run(p, fn, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal interface between the C ABI (api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fg8 {
+
+enum GemmMode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+
+// One GEMM problem as the kernels see it.  Per group g (expert or batch
+// entry): A rows [M][K], B [N][K], D [M][N].  Scales are FP32 (block-scaled
+// path) or E8M0 bytes (MX path); their strides follow fg8.h.
+struct GemmProblem {
+  const uint8_t* a;
+  const void* sa;
+  const uint8_t* b;
+  const void* sb;
+  void* d;
+  int out_bf16;
+  int mx;                       // 1: E8M0 scales through the scaled MFMA
+  int mode;                     // GemmMode
+  int64_t M, N, K;              // M = rows per group (dense m, contiguous m_total, masked cap)
+  int groups;                   // experts (masked / contiguous) or 1
+  const int32_t* block_expert;  // contiguous: expert of each 128-row block
+  const int32_t* valid;         // masked: live rows per group (NULL = all M)
+  // split-K (dense only)
+  int splits;
+  float* ws_partial;
+  int32_t* ws_counters;
+};
+
+// Split-K workspace layout: a fixed header of per-tile arrival counters
+// (split-K is only used when there are at most kSplitKMaxTiles tiles), then
+// the FP32 partial tiles.  Because the header never moves, a workspace can be
+// reused across shapes: every completed call leaves all counters at zero and
+// partial sums never land on them.
+constexpr int kSplitKMaxTiles = 1024;
+constexpr size_t kSplitKCounterBytes = kSplitKMaxTiles * sizeof(int32_t);
+
+struct TileChoice {
+  int cfg;      // index into the compiled tile configurations
+  int bm, bn;
+  int splits;
+  int grid;
+};
+
+TileChoice choose_tiles(const GemmProblem& p, int num_cus);
+size_t splitk_workspace_bytes(int64_t m, int64_t n, int64_t k, int num_cus);
+hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t stream);
+
+hipError_t launch_quantize(const float* x, int64_t batch, int64_t rows, int64_t cols, int kind,
+                           uint8_t* q, void* scales, hipStream_t stream);
+
+int device_cu_count();
+
+}  // namespace fg8

@@ -1,0 +1,604 @@
+// Block-scaled FP8 GEMM with two-level accumulation, its MoE grouped forms,
+// and the MXFP8 variant, for gfx950.
+//
+// What is computed: D[m][n] = sum_kb (sa[kb][m] * sb[n/128][kb]) *
+// sum_{k in kb} qa[m][k] * qb[n][k].  The inner sum over one 128-wide K block
+// is one v_mfma_f32_16x16x128_f8f6f4 (FP8 x FP8 -> FP32); the outer sum is an
+// FP32 fused multiply-add per K block in registers.  That is the two-level
+// accumulation of DeepGEMM (release news, ctol-kr.com, section 1 "FP8": the
+// tensor-core FP8 partial sums are promoted into FP32 accumulators on the
+// CUDA cores at a fixed interval); here the interval is one scale block, which
+// the per-128 scales force.  The MXFP8 path (aitrends.kr B200 article, MXFP8
+// section) instead hands each lane's E8M0 byte to
+// v_mfma_scale_f32_16x16x128_f8f6f4 and accumulates straight through K.
+//
+// Work decomposition (one wavefront = 64 lanes, 4 waves per workgroup):
+//   * a workgroup owns a BM x BN output tile; waves split it WAVES_M x WAVES_N;
+//     each wave holds its (BM/WAVES_M) x (BN/WAVES_N) FP32 accumulators in
+//     VGPRs as 16x16 MFMA tiles;
+//   * per 128-wide K block the A and B tiles (BM x 128 and BN x 128 bytes) and
+//     their scales are copied from global memory straight into LDS with
+//     global_load_lds_dwordx4 / _dword (no staging registers), STAGES blocks
+//     in flight;
+//   * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
+//     (r & 7) ^ ((r >> 3) & 1), so the MFMA operand reads (ds_read_b128 of
+//     one chunk from 16 consecutive rows) hit distinct banks;
+//   * a persistent grid walks a linear list of work units: dense tiles
+//     (optionally split along K with a deterministic last-arriver reduction),
+//     contiguous-layout tiles whose expert comes from block_expert, or
+//     masked-layout tiles enumerated from the device-side valid counts.
+//
+// Lane layout (measured on gfx950 by the probe tests): in the 16x16x128 MFMA
+// lane l = i + 16 g holds row i of A (column i of B) with K = 16 g .. 16 g + 15
+// in bytes 0-15 and K = 64 + 16 g .. +15 in bytes 16-31; result register v of
+// lane l is D[4 (l / 16) + v][l % 16]; with scales, the E8M0 byte of lane
+// i + 16 c scales K block c (32 elements) of row i.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "fg8_device.h"
+#include "fg8_internal.h"
+
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is written by the LDS-DMA asm
+
+namespace fg8 {
+
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int BM_, int BN_, int WAVES_M_, int STAGES_, int OCC_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = 4 / WAVES_M_;
+  static constexpr int STAGES = STAGES_, OCC = OCC_;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  // One stage: A tile | B tile | A row scales (FP32 sa or E8M0 dwords) |
+  // B row scales (E8M0 dwords, MX only) | one B-block scale per wave (FP32).
+  static constexpr int A_BYTES = BM * kGroup, B_BYTES = BN * kGroup;
+  static constexpr int SA_BYTES = BM * 4, SB_BYTES = BN * 4, SBW_BYTES = 16;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES + SBW_BYTES;
+  static constexpr int A_LOADS = BM / 32;   // 16-byte LDS-DMA loads per wave per stage
+  static constexpr int B_LOADS = BN / 32;
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile sides must be multiples of 32");
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
+  static_assert(WN <= 128 && (128 % WN) == 0, "a wave's columns must sit in one 128-block");
+  static_assert(BM / 4 <= 64 && BN / 4 <= 64, "one scale load per wave must cover its rows");
+  static_assert(STAGES >= 2, "need at least double buffering");
+  static_assert(STAGE_BYTES % 16 == 0, "stages stay 16-byte aligned");
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int L, int MAXN>
+__device__ __forceinline__ void wait_stages_after(int pending) {
+  // Wait until at most `pending` later stages (L loads each) are outstanding.
+  if constexpr (MAXN <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (pending >= MAXN) wait_vmcnt<L * MAXN>();
+    else wait_stages_after<L, MAXN - 1>(pending);
+  }
+}
+
+// Global -> LDS copies without staging registers (global_load_lds_*).
+// Lane i of the wave writes its 16 (or 4) bytes at LDS address m0 + 16 i
+// (4 i); the global address is the uniform base plus the lane's 32-bit
+// offset.  They are issued from inline assembly so that the compiler does not
+// guard every later LDS read with a wait for all of them: the kernel counts
+// these loads itself (wait_vmcnt) and orders LDS use with barriers.  The
+// instructions write no VGPR.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+template <class T>
+__device__ __forceinline__ T uniform(T v) {
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  } else {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+  }
+}
+
+// One MFMA operand fragment: 16 rows starting at tile row r0.
+__device__ __forceinline__ v8i load_frag(const uint8_t* tile, int r0, int lane) {
+  const int r = r0 + (lane & 15), g = lane >> 4, s = swz(r);
+  const uint8_t* row = tile + r * kGroup;
+  const int4 lo = *reinterpret_cast<const int4*>(row + ((g ^ s) << 4));
+  const int4 hi = *reinterpret_cast<const int4*>(row + (((g + 4) ^ s) << 4));
+  v8i f;
+  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  return f;
+}
+
+// Split-K partials are published with agent-scope relaxed atomic stores
+// (written through to the point of coherence shared by all XCDs) and read back
+// with agent-scope relaxed atomic loads; a vmcnt(0) wait orders them before
+// the arrival counter, so no L2 write-back fence is needed.
+__device__ __forceinline__ void store_coherent(float* p, v4f v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    __hip_atomic_store(p + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ v4f load_coherent(const float* p) {
+  v4f v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v[i] = __hip_atomic_load(const_cast<float*>(p) + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+__device__ __forceinline__ void wait_all_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+struct Unit {
+  int g;            // group (expert)
+  int64_t m0, n0;   // tile origin inside the group
+  int kb0, kb1;     // K-block range
+  int split, tile;  // split-K index and flat tile id
+  int rows;         // live rows of this group (dense: M)
+};
+
+template <class C, bool MX, int MODE>
+__global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGES * C::STAGE_BYTES];
+  __shared__ int tile_prefix[MODE == kMasked ? 1025 : 1];
+  __shared__ int flag;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
+  const int wm0 = wm * C::WM, wn0 = wn * C::WN;
+  const int64_t M = p.M, N = p.N, K = p.K;
+  const int KB = (int)(K / kGroup);
+  const int n_tiles = (int)((N + C::BN - 1) / C::BN);
+  const int splits = MODE == kDense ? p.splits : 1;
+  const int64_t nb_blocks = (N + kGroup - 1) / kGroup;
+
+  // ---- enumerate work units
+  int total;
+  if constexpr (MODE == kMasked) {
+    // tiles per group from the device-side counts; exclusive prefix in LDS.
+    const int G = p.groups;
+    int local[4];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid * 4 + j;
+      int v = 0;
+      if (e < G) {
+        const int64_t rows = p.valid ? (int64_t)p.valid[e] : M;
+        v = (int)((rows + C::BM - 1) / C::BM) * n_tiles;
+      }
+      local[j] = v;
+      sum += v;
+    }
+    // block-wide exclusive scan of the per-thread sums
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += t;
+    }
+    __shared__ int wave_tot[4];
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wave_tot[w];
+    int run = base + incl - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid * 4 + j;
+      if (e < G) tile_prefix[e] = run;
+      run += local[j];
+    }
+    if (tid == 255) tile_prefix[G] = run;   // grand total (G <= 1024)
+    __syncthreads();
+    total = tile_prefix[G];
+  } else {
+    total = (int)((M + C::BM - 1) / C::BM) * n_tiles * splits;
+  }
+
+  v4f acc[C::TM][C::TN];
+  const uint32_t lds0 = lds_addr(smem);
+
+  for (int u = blockIdx.x; u < total; u += gridDim.x) {
+    // ---- decode the unit
+    Unit w;
+    if constexpr (MODE == kMasked) {
+      int lo = 0, hi = p.groups - 1;   // last group with prefix <= u
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tile_prefix[mid] <= u) lo = mid; else hi = mid - 1;
+      }
+      const int t = u - tile_prefix[lo];
+      w.g = lo;
+      w.m0 = (int64_t)(t / n_tiles) * C::BM;
+      w.n0 = (int64_t)(t % n_tiles) * C::BN;
+      w.kb0 = 0; w.kb1 = KB; w.split = 0; w.tile = u;
+      w.rows = p.valid ? p.valid[lo] : (int)M;
+    } else {
+      const int t = u / splits;
+      w.split = u % splits;
+      w.tile = t;
+      w.m0 = (int64_t)(t / n_tiles) * C::BM;
+      w.n0 = (int64_t)(t % n_tiles) * C::BN;
+      w.kb0 = (int)((int64_t)w.split * KB / splits);
+      w.kb1 = (int)((int64_t)(w.split + 1) * KB / splits);
+      w.rows = (int)M;
+      w.g = 0;
+      if constexpr (MODE == kContiguous) w.g = p.block_expert[w.m0 / kGroup];
+    }
+    w.g = uniform(w.g);
+    w.m0 = uniform(w.m0);
+    w.n0 = uniform(w.n0);
+    w.kb0 = uniform(w.kb0);
+    w.kb1 = uniform(w.kb1);
+    w.rows = uniform(w.rows);
+
+    const uint8_t* ga;
+    const uint8_t* gb = p.b;
+    const float* gsa = nullptr;
+    const float* gsb = nullptr;
+    const uint8_t* gea = nullptr;
+    const uint8_t* geb = nullptr;
+    if constexpr (MODE == kMasked) {
+      ga = p.a + (int64_t)w.g * M * K;
+      gb = p.b + (int64_t)w.g * N * K;
+      if constexpr (MX) {
+        gea = (const uint8_t*)p.sa + (int64_t)w.g * M * (K / kMxBlock);
+        geb = (const uint8_t*)p.sb + (int64_t)w.g * N * (K / kMxBlock);
+      } else {
+        gsa = (const float*)p.sa + (int64_t)w.g * KB * M;
+        gsb = (const float*)p.sb + (int64_t)w.g * nb_blocks * KB;
+      }
+    } else {
+      ga = p.a;
+      gsa = (const float*)p.sa;
+      gb = p.b + (int64_t)w.g * N * K;
+      gsb = (const float*)p.sb + (int64_t)w.g * nb_blocks * KB;
+    }
+
+    // every wave must be done with the LDS stages of the previous unit
+    __syncthreads();
+
+    const int last_row = w.rows - 1;
+    const bool wave_live = (w.m0 + wm0) < w.rows;   // masked: rows past the count are skipped
+
+    // Per-lane byte offsets of the LDS-DMA sources, relative to the tile's
+    // first row (fixed for the unit).  Rows past the live count (or past N)
+    // are clamped to the last live row: they are read but never stored.
+    uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i) {
+      const int r = wave * (C::BM / 4) + i * 8 + (lane >> 3);
+      const int64_t gr = w.m0 + r < last_row ? w.m0 + r : last_row;
+      a_off[i] = (uint32_t)((gr - w.m0) * K + (((lane & 7) ^ swz(r)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_LOADS; ++i) {
+      const int r = wave * (C::BN / 4) + i * 8 + (lane >> 3);
+      const int64_t gr = w.n0 + r < N - 1 ? w.n0 + r : N - 1;
+      b_off[i] = (uint32_t)((gr - w.n0) * K + (((lane & 7) ^ swz(r)) << 4));
+    }
+    uint32_t sa_off, sb_off = 0;
+    {
+      const int64_t r = w.m0 + wave * (C::BM / 4) + lane;
+      const int64_t gr = r < last_row ? r : last_row;
+      sa_off = (uint32_t)((gr - w.m0) * (MX ? K / kMxBlock : 4));
+      if constexpr (MX) {
+        const int64_t rb = w.n0 + wave * (C::BN / 4) + lane;
+        sb_off = (uint32_t)(((rb < N - 1 ? rb : N - 1) - w.n0) * (K / kMxBlock));
+      }
+    }
+    // the B-block scale row of this wave's columns (FP32 path)
+    const int64_t nbw0 = (w.n0 + wn0) / kGroup;
+    const int64_t nbw = nbw0 < nb_blocks - 1 ? nbw0 : nb_blocks - 1;
+    const float* sb_row = MX ? nullptr : gsb + nbw * KB;
+    const uint8_t* a_tile = ga + w.m0 * K;
+    const uint8_t* b_tile = gb + w.n0 * K;
+    auto issue_stage = [&](int kb, int stage) {
+      const uint32_t st = uniform(lds0 + (uint32_t)(stage * C::STAGE_BYTES));
+      const uint8_t* ab = uniform(a_tile + (int64_t)kb * kGroup);
+      const uint8_t* bb = uniform(b_tile + (int64_t)kb * kGroup);
+#pragma unroll
+      for (int i = 0; i < C::A_LOADS; ++i)
+        dma16(ab, a_off[i], uniform(st + (uint32_t)((wave * (C::BM / 4) + i * 8) * kGroup)));
+#pragma unroll
+      for (int i = 0; i < C::B_LOADS; ++i)
+        dma16(bb, b_off[i],
+              uniform(st + (uint32_t)(C::A_BYTES + (wave * (C::BN / 4) + i * 8) * kGroup)));
+      const uint32_t sst = st + C::A_BYTES + C::B_BYTES;
+      if constexpr (MX) {
+        // E8M0 bytes of K block kb for each tile row: one dword per row.
+        const uint8_t* eab = uniform(gea + w.m0 * (K / kMxBlock) + kb * 4);
+        const uint8_t* ebb = uniform(geb + w.n0 * (K / kMxBlock) + kb * 4);
+        const uint32_t la = uniform(sst + (uint32_t)(wave * (C::BM / 4) * 4));
+        const uint32_t lb = uniform(sst + (uint32_t)(C::SA_BYTES + wave * (C::BN / 4) * 4));
+        if (lane < C::BM / 4) dma4(eab, sa_off, la);
+        if (lane < C::BN / 4) dma4(ebb, sb_off, lb);
+      } else {
+        const float* sab = uniform(gsa + (int64_t)kb * M + w.m0);
+        const uint32_t la = uniform(sst + (uint32_t)(wave * (C::BM / 4) * 4));
+        if (lane < C::BM / 4) dma4(sab, sa_off, la);
+        // this wave's B-block scale for K block kb, one lane
+        const float* sbp = uniform(sb_row + kb);
+        const uint32_t lw = uniform(sst + (uint32_t)(C::SA_BYTES + C::SB_BYTES + wave * 4));
+        if (lane == 0) dma4(sbp, 0u, lw);
+      }
+    };
+    constexpr int LOADS = C::A_LOADS + C::B_LOADS + 2;
+
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // ---- prologue: STAGES-1 K blocks in flight
+    const int nkb = w.kb1 - w.kb0;
+#pragma unroll
+    for (int s = 0; s < C::STAGES - 1; ++s)
+      if (s < nkb) issue_stage(w.kb0 + s, s);
+
+    // ---- main loop
+    for (int i = 0; i < nkb; ++i) {
+      const int kb = w.kb0 + i;
+      const int later = min(C::STAGES - 2, nkb - 1 - i);   // stages issued after kb
+      wait_stages_after<LOADS, C::STAGES - 2>(later);
+      __syncthreads();
+      if (i + C::STAGES - 1 < nkb) issue_stage(kb + C::STAGES - 1, (i + C::STAGES - 1) % C::STAGES);
+
+      if (wave_live) {
+        const uint8_t* st = smem + (i % C::STAGES) * C::STAGE_BYTES;
+        const uint8_t* As = st;
+        const uint8_t* Bs = st + C::A_BYTES;
+        const uint8_t* Ss = st + C::A_BYTES + C::B_BYTES;
+        v8i fa[C::TM];
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm) fa[tm] = load_frag(As, wm0 + tm * 16, lane);
+        if constexpr (MX) {
+          int sA[C::TM];
+#pragma unroll
+          for (int tm = 0; tm < C::TM; ++tm)
+            sA[tm] = (int)(reinterpret_cast<const uint32_t*>(Ss)[wm0 + tm * 16 + (lane & 15)] >>
+                           (8 * (lane >> 4)));
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn) {
+            const v8i fb = load_frag(Bs, wn0 + tn * 16, lane);
+            const int sB = (int)(reinterpret_cast<const uint32_t*>(Ss + C::SA_BYTES)
+                                     [wn0 + tn * 16 + (lane & 15)] >> (8 * (lane >> 4)));
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm)
+              acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  fa[tm], fb, acc[tm][tn], 0, 0, 0, sA[tm], 0, sB);
+          }
+        } else {
+          const float sbv =
+              *reinterpret_cast<const float*>(Ss + C::SA_BYTES + C::SB_BYTES + wave * 4);
+          v4f sc[C::TM];
+#pragma unroll
+          for (int tm = 0; tm < C::TM; ++tm) {
+            const float4 s4 = *reinterpret_cast<const float4*>(
+                Ss + (wm0 + tm * 16 + 4 * (lane >> 4)) * 4);
+            sc[tm] = v4f{s4.x * sbv, s4.y * sbv, s4.z * sbv, s4.w * sbv};
+          }
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn) {
+            const v8i fb = load_frag(Bs, wn0 + tn * 16, lane);
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm) {
+              const v4f z = {0.f, 0.f, 0.f, 0.f};
+              const v4f part =
+                  __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[tm], fb, z, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+              for (int v = 0; v < 4; ++v) acc[tm][tn][v] = fmaf(part[v], sc[tm][v], acc[tm][tn][v]);
+            }
+          }
+        }
+      }
+    }
+
+    // ---- split-K: deterministic last-arriver reduction through the workspace
+    if (MODE == kDense && splits > 1) {
+      float* part = p.ws_partial + ((int64_t)w.tile * splits + w.split) * (C::BM * C::BN);
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+          const int idx = ((wave * C::TM + tm) * C::TN + tn) * 64 + lane;
+          store_coherent(part + 4 * idx, acc[tm][tn]);
+        }
+      wait_all_memory();        // this thread's partials have reached the coherence point
+      __syncthreads();          // ... and every other thread's
+      if (tid == 0)
+        flag = __hip_atomic_fetch_add(p.ws_counters + w.tile, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+      __syncthreads();
+      if (!flag) continue;
+      const float* base = p.ws_partial + (int64_t)w.tile * splits * (C::BM * C::BN);
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+          const int idx = ((wave * C::TM + tm) * C::TN + tn) * 64 + lane;
+          v4f sum = {0.f, 0.f, 0.f, 0.f};
+          for (int s = 0; s < splits; ++s)   // fixed order: bitwise reproducible
+            sum += s == w.split ? acc[tm][tn] : load_coherent(base + s * (C::BM * C::BN) + 4 * idx);
+          acc[tm][tn] = sum;
+        }
+      if (tid == 0)
+        __hip_atomic_store(p.ws_counters + w.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- epilogue: FP32 or BF16 (RNE), rows past the live count and columns
+    // past N are not written
+    if (wave_live) {
+      const int64_t d_off = MODE == kMasked ? (int64_t)w.g * M * N : 0;
+#pragma unroll
+      for (int tm = 0; tm < C::TM; ++tm) {
+#pragma unroll
+        for (int tn = 0; tn < C::TN; ++tn) {
+          const int64_t col = w.n0 + wn0 + tn * 16 + (lane & 15);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int64_t row = w.m0 + wm0 + tm * 16 + 4 * (lane >> 4) + v;
+            if (row < w.rows && col < N) {
+              const int64_t o = d_off + row * N + col;
+              if (p.out_bf16)
+                reinterpret_cast<uint16_t*>(p.d)[o] = f32_to_bf16(acc[tm][tn][v]);
+              else
+                reinterpret_cast<float*>(p.d)[o] = acc[tm][tn][v];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ configs
+// Name                         BM   BN WAVES_M STAGES OCC      wave tile
+using CfgBig = Cfg<256, 128, 4, 3, 1>;       // 64 x 128
+using CfgWide = Cfg<128, 256, 2, 3, 1>;      // 64 x 128 (contiguous needs BM <= 128)
+using CfgS32 = Cfg<64, 32, 2, 8, 1>;         // 32 x 16, deep pipeline
+using CfgS32x2 = Cfg<64, 32, 2, 5, 2>;       // 32 x 16, two workgroups per CU
+using CfgS64 = Cfg<64, 64, 1, 6, 1>;         // 64 x 16
+using CfgS128 = Cfg<64, 128, 1, 5, 1>;       // 64 x 32
+using CfgM64 = Cfg<128, 64, 2, 5, 1>;        // 64 x 32
+using CfgM32 = Cfg<128, 32, 4, 6, 1>;        // 32 x 32
+
+struct CfgInfo {
+  int bm, bn, occ;
+};
+static const CfgInfo kCfgs[] = {
+    {CfgBig::BM, CfgBig::BN, CfgBig::OCC},       {CfgWide::BM, CfgWide::BN, CfgWide::OCC},
+    {CfgS32::BM, CfgS32::BN, CfgS32::OCC},       {CfgS32x2::BM, CfgS32x2::BN, CfgS32x2::OCC},
+    {CfgS64::BM, CfgS64::BN, CfgS64::OCC},       {CfgS128::BM, CfgS128::BN, CfgS128::OCC},
+    {CfgM64::BM, CfgM64::BN, CfgM64::OCC},       {CfgM32::BM, CfgM32::BN, CfgM32::OCC},
+};
+enum CfgId {
+  kCfgBig = 0, kCfgWide, kCfgS32, kCfgS32x2, kCfgS64, kCfgS128, kCfgM64, kCfgM32, kNumCfgs
+};
+
+int device_cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Split count for a dense problem: enough (tile, split) units to give every
+// workgroup slot one, keeping at least two K blocks per split.
+static int dense_splits(int64_t tiles, int64_t kb, int slots) {
+  if (tiles * 2 > slots || tiles > kSplitKMaxTiles) return 1;
+  int64_t s = slots / tiles;
+  if (s > kb / 2) s = kb / 2;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+// FG8_TILE_OVERRIDE="cfg[,splits]" forces a compiled tile configuration (and
+// split count) for dense problems: a tuning hook, not needed for correctness.
+static bool tile_override(int* cfg, int* splits) {
+  const char* e = getenv("FG8_TILE_OVERRIDE");
+  if (!e || !*e) return false;
+  int c = -1, s = 0;
+  if (sscanf(e, "%d,%d", &c, &s) < 1 || c < 0 || c >= kNumCfgs) return false;
+  *cfg = c;
+  *splits = s;
+  return true;
+}
+
+TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
+  TileChoice t{};
+  int forced_splits = 0;
+  bool forced = false;
+  if (p.mode == kContiguous) t.cfg = kCfgWide;
+  else if (p.mode == kDense && (forced = tile_override(&t.cfg, &forced_splits))) {}
+  else if (p.mode == kDense && p.M <= 64) t.cfg = kCfgS32;
+  else t.cfg = kCfgBig;
+  t.bm = kCfgs[t.cfg].bm;
+  t.bn = kCfgs[t.cfg].bn;
+  const int slots = num_cus * kCfgs[t.cfg].occ;
+  const int64_t n_tiles = (p.N + t.bn - 1) / t.bn;
+  const int64_t KB = p.K / kGroup;
+  int64_t units;
+  t.splits = 1;
+  if (p.mode == kMasked) {
+    units = (int64_t)p.groups * ((p.M + t.bm - 1) / t.bm) * n_tiles;   // upper bound
+  } else {
+    const int64_t tiles = ((p.M + t.bm - 1) / t.bm) * n_tiles;
+    if (p.mode == kDense) {
+      t.splits = dense_splits(tiles, KB, slots);
+      if (forced && forced_splits > 0 && tiles <= kSplitKMaxTiles)
+        t.splits = (int)(forced_splits < KB ? forced_splits : KB);
+    }
+    units = tiles * t.splits;
+  }
+  t.grid = (int)(units < slots ? units : slots);
+  if (t.grid < 1) t.grid = 1;
+  return t;
+}
+
+size_t splitk_workspace_bytes(int64_t m, int64_t n, int64_t k, int num_cus) {
+  GemmProblem p{};
+  p.mode = kDense; p.M = m; p.N = n; p.K = k; p.groups = 1;
+  const TileChoice t = choose_tiles(p, num_cus);
+  if (t.splits <= 1) return 0;
+  const int64_t tiles = ((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn);
+  return kSplitKCounterBytes + (size_t)tiles * t.splits * t.bm * t.bn * sizeof(float);
+}
+
+template <class C, bool MX, int MODE>
+static hipError_t launch(const GemmProblem& p, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_kernel<C, MX, MODE>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
+  p.splits = t.splits;
+  switch (p.mode) {
+    case kDense:
+      switch (t.cfg) {
+        case kCfgWide: return launch<CfgWide, false, kDense>(p, t.grid, s);
+        case kCfgS32: return launch<CfgS32, false, kDense>(p, t.grid, s);
+        case kCfgS32x2: return launch<CfgS32x2, false, kDense>(p, t.grid, s);
+        case kCfgS64: return launch<CfgS64, false, kDense>(p, t.grid, s);
+        case kCfgS128: return launch<CfgS128, false, kDense>(p, t.grid, s);
+        case kCfgM64: return launch<CfgM64, false, kDense>(p, t.grid, s);
+        case kCfgM32: return launch<CfgM32, false, kDense>(p, t.grid, s);
+        default: return launch<CfgBig, false, kDense>(p, t.grid, s);
+      }
+    case kContiguous:
+      return launch<CfgWide, false, kContiguous>(p, t.grid, s);
+    default:
+      if (p.mx) return launch<CfgBig, true, kMasked>(p, t.grid, s);
+      return launch<CfgBig, false, kMasked>(p, t.grid, s);
+  }
+}
+
+}  // namespace fg8

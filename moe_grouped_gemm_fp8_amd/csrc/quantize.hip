@@ -1,0 +1,151 @@
+// FP32 -> e4m3 quantization with fine-grained scales.
+//
+// Scale then convert: the FP32 tensor is multiplied by a scaling factor and
+// turned into FP8 (cuda-deepseek blog, hrletsgo.me, list item 5), per tile
+// rather than per tensor as that blog's own comments ask for, at the
+// granularities DeepGEMM uses (1x128 activation groups, 128x128 weight
+// blocks), plus MX blocks of 32 elements sharing one power-of-two exponent
+// (aitrends.kr B200 article, MXFP8 glossary entry).
+//
+// All three kernels are HBM-bound streams (4 B read + ~1.03 B written per
+// element): float4 loads, amax by butterfly exchanges inside the lanes that
+// hold one group, one packed 4-byte store of codes per lane.  Results are
+// bit-exact with the format rules in fg8.h: the scale is the correctly
+// rounded float32 quotient amax / 448, elements use a correctly rounded
+// float32 division by it, and the MX exponent comes straight from the float
+// bits of amax.
+#include "fg8_device.h"
+#include "fg8_internal.h"
+
+namespace fg8 {
+
+// ---------------------------------------------------------------- 1 x 128
+// Block: 256 threads = 4 waves; one block covers 32 rows x 128 columns (one
+// K group).  Each wave handles 8 rows, 2 rows per step: lanes 0-31 one row,
+// lanes 32-63 the next, 4 floats per lane.  Scales are written K-block major,
+// so the 32 scales of a block are contiguous.
+constexpr int kQRowsPerBlock = 32;
+
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const float* __restrict__ x,
+                                                          uint8_t* __restrict__ q,
+                                                          float* __restrict__ s, int64_t rows,
+                                                          int64_t cols) {
+  const int64_t b = blockIdx.z;
+  const int kb = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t kblocks = cols / kGroup;
+  const float* xb = x + b * rows * cols;
+  uint8_t* qb = q + b * rows * cols;
+  float* sb = s + b * kblocks * rows + (int64_t)kb * rows;
+  const int64_t row0 = (int64_t)blockIdx.x * kQRowsPerBlock + wave * 8 + (lane >> 5);
+  const int64_t col = (int64_t)kb * kGroup + (lane & 31) * 4;
+
+  float4 v[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int64_t r = row0 + 2 * st;
+    v[st] = r < rows ? *reinterpret_cast<const float4*>(xb + r * cols + col)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int64_t r = row0 + 2 * st;
+    const float amax = group_max<32>(abs_max4(v[st]));
+    const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
+    if (r < rows) {
+      const float4 y = make_float4(v[st].x / sc, v[st].y / sc, v[st].z / sc, v[st].w / sc);
+      *reinterpret_cast<uint32_t*>(qb + r * cols + col) = pack4_e4m3(y);
+      if ((lane & 31) == 0) sb[r] = sc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 128 x 128
+// Block: 256 threads over one 128x128 block.  Thread t owns column chunk
+// (t % 32) * 4 of rows t / 32 + 8 i, i = 0..15: 16 float4 in registers, the
+// amax is reduced across the wave and then across the 4 waves through LDS.
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restrict__ x,
+                                                            uint8_t* __restrict__ q,
+                                                            float* __restrict__ s, int64_t rows,
+                                                            int64_t cols) {
+  __shared__ float wave_max[4];
+  const int64_t b = blockIdx.z;
+  const int cb = blockIdx.x, rb = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t kblocks = cols / kGroup;
+  const int64_t rblocks = (rows + kGroup - 1) / kGroup;
+  const float* xb = x + b * rows * cols;
+  uint8_t* qb = q + b * rows * cols;
+  const int64_t col = (int64_t)cb * kGroup + (tid & 31) * 4;
+  const int64_t r0 = (int64_t)rb * kGroup + (tid >> 5);
+
+  float4 v[16];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + 8 * i;
+    v[i] = r < rows ? *reinterpret_cast<const float4*>(xb + r * cols + col)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    m = fmaxf(m, abs_max4(v[i]));
+  }
+  m = group_max<64>(m);
+  if ((tid & 63) == 0) wave_max[tid >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = r0 + 8 * i;
+    if (r < rows) {
+      const float4 y = make_float4(v[i].x / sc, v[i].y / sc, v[i].z / sc, v[i].w / sc);
+      *reinterpret_cast<uint32_t*>(qb + r * cols + col) = pack4_e4m3(y);
+    }
+  }
+  if (tid == 0) s[b * rblocks * kblocks + (int64_t)rb * kblocks + cb] = sc;
+}
+
+// ---------------------------------------------------------------- MX 1 x 32
+// The tensor is a flat run of 32-element blocks (cols % 32 == 0, so no block
+// crosses a row) and the E8M0 array is indexed by the same block number.
+// Eight lanes hold one block; a grid-stride loop walks the blocks.
+__global__ __launch_bounds__(256) void quant_mx_kernel(const float* __restrict__ x,
+                                                       uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ e, int64_t nblocks) {
+  const int64_t stride = (int64_t)gridDim.x * 32;   // blocks per grid sweep (256 threads / 8)
+  const int sub = threadIdx.x & 7;
+  for (int64_t blk = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); blk < nblocks; blk += stride) {
+    const float4 v = *reinterpret_cast<const float4*>(x + blk * kMxBlock + sub * 4);
+    const float amax = group_max<8>(abs_max4(v));
+    // floor(log2 amax) - 8 from the exponent field; subnormal or zero amax
+    // lands below -127 and is clamped there with the largest normal result.
+    const int expf = (int)((__float_as_uint(amax) >> 23) & 0xFF);
+    const int E = max(expf - 127 - 8, -127);
+    const float inv = __uint_as_float((uint32_t)(127 - E) << 23);   // 2^-E, exact
+    const float4 y = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
+    *reinterpret_cast<uint32_t*>(q + blk * kMxBlock + sub * 4) = pack4_e4m3(y);
+    if (sub == 0) e[blk] = (uint8_t)(E + 127);
+  }
+}
+
+hipError_t launch_quantize(const float* x, int64_t batch, int64_t rows, int64_t cols, int kind,
+                           uint8_t* q, void* scales, hipStream_t stream) {
+  if (kind == 0) {
+    dim3 grid((unsigned)((rows + kQRowsPerBlock - 1) / kQRowsPerBlock), (unsigned)(cols / kGroup),
+              (unsigned)batch);
+    hipLaunchKernelGGL(quant_1x128_kernel, grid, dim3(256), 0, stream, x, q, (float*)scales, rows,
+                       cols);
+  } else if (kind == 1) {
+    dim3 grid((unsigned)(cols / kGroup), (unsigned)((rows + kGroup - 1) / kGroup), (unsigned)batch);
+    hipLaunchKernelGGL(quant_128x128_kernel, grid, dim3(256), 0, stream, x, q, (float*)scales,
+                       rows, cols);
+  } else {
+    const int64_t nblocks = batch * rows * cols / kMxBlock;
+    const int64_t want = (nblocks + 31) / 32;
+    const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+    hipLaunchKernelGGL(quant_mx_kernel, dim3(grid), dim3(256), 0, stream, x, q,
+                       (uint8_t*)scales, nblocks);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fg8

@@ -182,10 +182,15 @@ class MaskedCase:
     workload: int = 4
 
 
+def masked_case_counts(c: MaskedCase) -> np.ndarray:
+    """Per-expert valid counts ~ U{0..cap} (inclusive), int32 [E]."""
+    return rng(c.workload, 3).integers(0, c.cap, size=c.experts, endpoint=True).astype(np.int32)
+
+
 def masked_case(c: MaskedCase):
     """(valid [E] int32 in [0, cap], A [E, cap, K], B [E, N, K]).  Rows of A at
     or past valid[e] hold large finite junk."""
-    valid = rng(c.workload, 3).integers(0, c.cap, size=c.experts, endpoint=True).astype(np.int32)
+    valid = masked_case_counts(c)
     a = _normal(rng(c.workload, 0), (c.experts, c.cap, c.K))
     junk = rng(c.workload, 2)
     for e in range(c.experts):

@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: libfg8.so loads, exports every function that
+include/fg8.h declares, and rejects bad arguments with the documented status
+before launching anything (no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fg8.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:fg8_status|size_t|const char\*|int)\s+(\w+)\s*\(", text, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from moe_grouped_gemm_fp8_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libfg8.so is not built (run __graft_entry__.build())")
+    return _lib.lib()
+
+
+def test_header_lists_the_five_entry_points():
+    names = _declared()
+    for n in ("fp8_quantize", "gemm_fp8_blockscaled", "grouped_gemm_fp8_contiguous",
+              "grouped_gemm_fp8_masked", "gemm_mxfp8", "fg8_gemm_workspace_bytes",
+              "fg8_last_error", "fg8_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for n in _declared():
+        assert hasattr(L, n), f"{n} declared in fg8.h but not exported"
+    assert L.fg8_version() == 100
+
+
+P = ctypes.c_void_p
+
+
+def _fake(addr):
+    return P(addr)   # never dereferenced: validation fails before any launch
+
+
+def test_quantize_validation(L):
+    ok = _fake(0x10000)
+    assert L.fp8_quantize(None, 1, 1, 128, 0, ok, ok, None) == 1
+    assert b"x is NULL" in L.fg8_last_error()
+    assert L.fp8_quantize(_fake(0x10004), 1, 1, 128, 0, ok, ok, None) == 1
+    assert b"16-byte" in L.fg8_last_error()
+    assert L.fp8_quantize(ok, 1, 1, 130, 0, ok, ok, None) == 2
+    assert L.fp8_quantize(ok, 1, 1, 96, 1, ok, ok, None) == 2
+    assert L.fp8_quantize(ok, 0, 1, 128, 0, ok, ok, None) == 1
+    assert L.fp8_quantize(ok, 1, 1, 128, 7, ok, ok, None) == 1
+    assert b"scale kind" in L.fg8_last_error()
+
+
+def test_gemm_validation(L):
+    ok = _fake(0x10000)
+    f = L.gemm_fp8_blockscaled
+    assert f(ok, ok, ok, ok, None, 0, 64, 64, 256, None, 0, None) == 1
+    assert f(ok, ok, ok, ok, ok, 5, 64, 64, 256, None, 0, None) == 1
+    assert f(ok, ok, ok, ok, ok, 0, 0, 64, 256, None, 0, None) == 1
+    assert f(ok, ok, ok, ok, ok, 0, 64, 64, 200, None, 0, None) == 2
+    assert f(ok, ok, ok, ok, ok, 0, 64, 64, 64, None, 0, None) == 2
+    assert f(ok, ok, ok, ok, ok, 0, 64, 64, 32768, None, 0, None) == 2
+    # a split-K shape with no workspace is refused before launching
+    need = L.fg8_gemm_workspace_bytes(64, 2112, 7168)
+    assert need > 4096
+    assert f(ok, ok, ok, ok, ok, 0, 64, 2112, 7168, None, 0, None) == 1
+    assert b"workspace" in L.fg8_last_error()
+    assert f(ok, ok, ok, ok, ok, 0, 64, 2112, 7168, ok, need - 1, None) == 1
+
+
+def test_workspace_bytes_host_logic(L):
+    assert L.fg8_gemm_workspace_bytes(4096, 7168, 2048) == 0      # enough tiles: no split
+    assert L.fg8_gemm_workspace_bytes(64, 2112, 200) == 0         # invalid K
+    a = L.fg8_gemm_workspace_bytes(64, 2112, 7168)
+    assert (a - 4096) % (64 * 32 * 4) == 0                        # whole 64x32 FP32 tiles
+
+
+def test_grouped_validation(L):
+    ok = _fake(0x10000)
+    c = L.grouped_gemm_fp8_contiguous
+    assert c(ok, ok, ok, ok, None, ok, 0, 256, 64, 256, 4, None) == 1
+    assert c(ok, ok, ok, ok, ok, ok, 0, 200, 64, 256, 4, None) == 2
+    assert c(ok, ok, ok, ok, ok, ok, 0, 256, 64, 256, 0, None) == 1
+    m = L.grouped_gemm_fp8_masked
+    assert m(ok, ok, ok, ok, None, ok, 0, 4, 256, 64, 256, None) == 1
+    assert m(ok, ok, ok, ok, ok, ok, 0, 2000, 256, 64, 256, None) == 1
+    assert m(ok, ok, ok, ok, ok, ok, 0, 4, 256, 64, 100, None) == 2
+    x = L.gemm_mxfp8
+    assert x(ok, ok, ok, ok, None, ok, 0, 0, 64, 64, 256, None) == 1
+    assert x(ok, ok, ok, ok, _fake(0x10008), ok, 0, 2, 64, 64, 256, None) == 1
+    assert x(ok, ok, ok, ok, None, ok, 0, 2, 64, 64, 96, None) == 2

@@ -1,0 +1,264 @@
+"""MoE grouped GEMMs (contiguous and masked layouts) and the MXFP8 GEMM
+against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_fp8_amd as fg8
+from moe_grouped_gemm_fp8_amd import inputs
+from oracle import e4m3, gemm, scaling
+from parity import check_bf16, check_f32, ref_blockscaled, ref_mx
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL_F32 = np.float32(-12345.5)
+
+
+def _gpu(*arrays):
+    return [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in arrays]
+
+
+def _bits(d):
+    if d.dtype == torch.bfloat16:
+        return d.view(torch.int16).cpu().numpy().view(np.uint16)
+    return d.cpu().numpy()
+
+
+def _check(d, C, S, K, where, derived=True, F=0.0):
+    if d.dtype == np.uint16:
+        return check_bf16(d, C, S, K, where, S_flush=F)
+    return check_f32(d, C, S, K, where, derived=derived, S_flush=F)
+
+
+# ------------------------------------------------------------- contiguous
+def _small_contiguous(tokens=300, hidden=512, inter=384, experts=6, topk=2):
+    c = inputs.ContiguousCase(tokens=tokens, hidden=hidden, inter=inter, inter2=256,
+                              experts=experts, topk=topk, workload=31)
+    return c, inputs.contiguous_case(c)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(300, 512, 384, 6, 2), (700, 1024, 200, 9, 3)])
+def test_contiguous_small(dev, shape, out_dtype):
+    c, (lay, a1, w1, a2, w2) = _small_contiguous(*shape)
+    qa, sa = scaling.quantize_1x128(a1)
+    qb, sb = scaling.quantize_128x128(w1)
+    C, S = gemm.grouped_contiguous(qa, sa, qb, sb, lay.block_expert)
+    ta, tsa, tb, tsb, tbe = _gpu(qa, sa, qb, sb, lay.block_expert)
+    d = fg8.grouped_gemm_fp8_contiguous(ta, tsa, tb, tsb, tbe, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    F = np.zeros_like(C)
+    for e in range(c.experts):
+        rows = np.repeat(lay.block_expert == e, 128)
+        if rows.any():
+            F[rows] = ref_blockscaled(qa[rows], sa[:, rows], qb[e], sb[e])[2]
+    _check(_bits(d), C, S, c.hidden, "contiguous small", F=F)
+
+
+def test_contiguous_zero_expert_and_padding(dev):
+    """Experts with no rows have no blocks; padding rows of A are zero and come
+    out as exact zeros."""
+    routing = np.array([[0, 2], [2, 3], [0, 3]] * 50, np.int32)     # expert 1 unused
+    lay = inputs.contiguous_layout(routing, 5)                       # expert 4 unused too
+    assert lay.counts[1] == 0 and lay.counts[4] == 0
+    x = inputs._normal(inputs.rng(32, 0), (routing.shape[0], 256))
+    a = inputs.gather_rows(x, lay.row_token)
+    w = inputs._normal(inputs.rng(32, 1), (5, 160, 256), 256 ** -0.5)
+    qa, sa = scaling.quantize_1x128(a)
+    qb, sb = scaling.quantize_128x128(w)
+    ta, tsa, tb, tsb, tbe = _gpu(qa, sa, qb, sb, lay.block_expert)
+    d = fg8.grouped_gemm_fp8_contiguous(ta, tsa, tb, tsb, tbe, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    C, S = gemm.grouped_contiguous(qa, sa, qb, sb, lay.block_expert)
+    out = d.cpu().numpy()
+    check_f32(out, C, S, 256, "contiguous zero expert")
+    assert np.all(out[lay.row_token < 0] == 0)
+
+
+@pytest.mark.parametrize("which", ["w1", "w2"])
+def test_contiguous_full_size_sampled(dev, which):
+    """The MoE workload at full size (8192 tokens, top-8 of 32 experts, Zipf
+    popularity; W1 7168 -> 4096 and W2 2048 -> 7168).  The GPU quantizes and
+    multiplies everything; the oracle checks sampled rows of every expert
+    against two 128-column blocks, quantized by itself from the FP32 sources."""
+    c = inputs.ContiguousCase()
+    lay, a1, w1, a2, w2 = inputs.contiguous_case(c)
+    A, W = (a1, w1) if which == "w1" else (a2, w2)
+    del a1, w1, a2, w2
+    K = A.shape[1]
+    tA, tW = _gpu(A, W)
+    qa, sa = fg8.fp8_quantize(tA, "1x128")
+    qb, sb = fg8.fp8_quantize(tW, "128x128")
+    del tA, tW
+    tbe = torch.from_numpy(lay.block_expert).cuda()
+    d = fg8.grouped_gemm_fp8_contiguous(qa, sa, qb, sb, tbe, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    out = _bits(d)
+    g = np.random.default_rng(400)
+    N = W.shape[1]
+    nbs = g.choice(N // 128, 2, replace=False)
+    cols = np.concatenate([np.arange(nb * 128, nb * 128 + 128) for nb in nbs])
+    for e in range(c.experts):
+        blocks = np.nonzero(lay.block_expert == e)[0]
+        if blocks.size == 0:
+            continue
+        own = np.concatenate([np.arange(b * 128, b * 128 + 128) for b in blocks])
+        rows = np.unique(np.concatenate([own[:8], own[-1:], g.choice(own, 8)]))
+        qa_o, sa_o = scaling.quantize_1x128(A[rows])
+        Bq = [scaling.quantize_128x128(W[e, nb * 128:(nb + 1) * 128]) for nb in nbs]
+        qb_o = np.concatenate([q for q, _ in Bq])
+        sb_o = np.concatenate([s for _, s in Bq])      # one row of scales per block
+        C, S, F = ref_blockscaled(qa_o, sa_o, qb_o, sb_o)
+        check_bf16(out[np.ix_(rows, cols)], C, S, K, f"{which} expert {e}", S_flush=F)
+
+
+# ------------------------------------------------------------- masked
+def _masked_inputs(E, cap, N, K, workload=41, valid=None):
+    mc = inputs.MaskedCase(experts=E, cap=cap, N=N, K=K, workload=workload)
+    v, a, b = inputs.masked_case(mc)
+    if valid is not None:
+        v = np.asarray(valid, np.int32)
+    return v, a, b
+
+
+def _poison(qa, sa_or_e, valid, scale_axis_rows):
+    """Rows at or past the count hold NaN codes and NaN (or 0xFF) scales: the
+    kernel must never let them reach a stored value."""
+    qa = qa.copy()
+    s = sa_or_e.copy()
+    for e, v in enumerate(valid):
+        qa[e, v:] = 0x7F
+        if scale_axis_rows == "last":
+            s[e, :, v:] = np.nan
+        else:
+            s[e, v:] = 0xFF
+    return qa, s
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_masked_small(dev, out_dtype):
+    E, cap, N, K = 7, 96, 200, 512
+    valid = [0, 96, 1, 37, 64, 95, 50]
+    v, a, b = _masked_inputs(E, cap, N, K, valid=valid)
+    qa, sa = scaling.quantize_1x128(a)
+    qb, sb = scaling.quantize_128x128(b)
+    C, S = gemm.grouped_masked(qa, sa, qb, sb, v)
+    qa_p, sa_p = _poison(qa, sa, v, "last")
+    ta, tsa, tb, tsb, tv = _gpu(qa_p, sa_p, qb, sb, v)
+    out = torch.full((E, cap, N), float(SENTINEL_F32), dtype=out_dtype, device="cuda")
+    fg8.grouped_gemm_fp8_masked(ta, tsa, tb, tsb, tv, out=out)
+    torch.cuda.synchronize()
+    d = _bits(out)
+    sentinel = _bits(torch.full((1,), float(SENTINEL_F32), dtype=out_dtype))[0]
+    for e in range(E):
+        assert np.all(d[e, v[e]:] == sentinel), f"expert {e}: rows past the count were written"
+        if v[e]:
+            F = ref_blockscaled(qa[e, :v[e]], sa[e][:, :v[e]], qb[e], sb[e])[2]
+            _check(d[e, :v[e]], C[e, :v[e]], S[e, :v[e]], K, f"masked expert {e}", F=F)
+
+
+def test_masked_full_size_sampled(dev):
+    """16 experts x 256 rows, N=4096, K=7168, counts ~ U{0..256}: all columns
+    computed on the GPU, two 128-column blocks of every expert checked."""
+    mc = inputs.MaskedCase()
+    v, a, b = inputs.masked_case(mc)
+    ta, tb = _gpu(a, b)
+    qa, sa = fg8.fp8_quantize(ta, "1x128")
+    qb, sb = fg8.fp8_quantize(tb, "128x128")
+    del ta, tb
+    tv = torch.from_numpy(v).cuda()
+    out = torch.full((16, 256, 4096), float(SENTINEL_F32), dtype=torch.bfloat16, device="cuda")
+    fg8.grouped_gemm_fp8_masked(qa, sa, qb, sb, tv, out=out)
+    torch.cuda.synchronize()
+    d = _bits(out)
+    sentinel = _bits(torch.full((1,), float(SENTINEL_F32), dtype=torch.bfloat16))[0]
+    g = np.random.default_rng(401)
+    for e in range(16):
+        assert np.all(d[e, v[e]:] == sentinel)
+        if not v[e]:
+            continue
+        nbs = g.choice(32, 2, replace=False)
+        cols = np.concatenate([np.arange(nb * 128, nb * 128 + 128) for nb in nbs])
+        qa_o, sa_o = scaling.quantize_1x128(a[e, :v[e]])
+        Bq = [scaling.quantize_128x128(b[e, nb * 128:(nb + 1) * 128]) for nb in nbs]
+        C, S, F = ref_blockscaled(qa_o, sa_o, np.concatenate([q for q, _ in Bq]),
+                                  np.concatenate([s for _, s in Bq]))
+        check_bf16(d[e, :v[e]][:, cols], C, S, 7168, f"masked full expert {e}", S_flush=F)
+
+
+# ------------------------------------------------------------- MXFP8
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_mx_masked_small(dev, out_dtype):
+    E, cap, N, K = 5, 80, 160, 384
+    valid = [80, 0, 33, 1, 79]
+    v, a, b = _masked_inputs(E, cap, N, K, workload=42, valid=valid)
+    qa, ea = scaling.quantize_mx(a)
+    qb, eb = scaling.quantize_mx(b)
+    C, S = gemm.gemm_mx(qa, ea, qb, eb, v)
+    qa_p, ea_p = _poison(qa, ea, v, "rows")
+    ta, tea, tb, teb, tv = _gpu(qa_p, ea_p, qb, eb, v)
+    out = torch.full((E, cap, N), float(SENTINEL_F32), dtype=out_dtype, device="cuda")
+    fg8.gemm_mxfp8(ta, tea, tb, teb, tv, out=out)
+    torch.cuda.synchronize()
+    d = _bits(out)
+    sentinel = _bits(torch.full((1,), float(SENTINEL_F32), dtype=out_dtype))[0]
+    for e in range(E):
+        assert np.all(d[e, v[e]:] == sentinel)
+        if v[e]:
+            F = ref_mx(qa[e, :v[e]], ea[e, :v[e]], qb[e], eb[e])[2]
+            _check(d[e, :v[e]], C[e, :v[e]], S[e, :v[e]], K, f"mx expert {e}", derived=False, F=F)
+
+
+def test_mx_dense_and_exponent_spread(dev):
+    """valid_rows = NULL means every row; exponents spread over a wide range
+    (per-row magnitudes 2^-20 .. 2^20) exercise the E8M0 lane mapping."""
+    g = np.random.default_rng(402)
+    G, M, N, K = 2, 70, 150, 512
+    a = (g.standard_normal((G, M, K)) * 2.0 ** g.integers(-20, 20, (G, M, K // 32)).repeat(32, -1)).astype(np.float32)
+    b = (g.standard_normal((G, N, K)) * 2.0 ** g.integers(-20, 20, (G, N, K // 32)).repeat(32, -1)).astype(np.float32)
+    qa, ea = scaling.quantize_mx(a)
+    qb, eb = scaling.quantize_mx(b)
+    C, S = gemm.gemm_mx(qa, ea, qb, eb)
+    ta, tea, tb, teb = _gpu(qa, ea, qb, eb)
+    d = fg8.gemm_mxfp8(ta, tea, tb, teb, None, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    err = check_f32(d.cpu().numpy(), C, S, K, "mx dense", derived=False)
+    print(f"\nmx dense, exponent spread +-20: max |err|/S = {err:.2e}")
+
+
+def test_mx_masked_full_size_sampled(dev):
+    """The MXFP8 variant of the masked workload: same FP32 sources, 1x32 E8M0
+    scales for A and B, quantized on the GPU; sampled columns checked."""
+    mc = inputs.MaskedCase()
+    v, a, b = inputs.masked_case(mc)
+    ta, tb = _gpu(a, b)
+    qa, ea = fg8.fp8_quantize(ta, "mx")
+    qb, eb = fg8.fp8_quantize(tb, "mx")
+    del ta, tb
+    tv = torch.from_numpy(v).cuda()
+    out = torch.full((16, 256, 4096), float(SENTINEL_F32), dtype=torch.bfloat16, device="cuda")
+    fg8.gemm_mxfp8(qa, ea, qb, eb, tv, out=out)
+    torch.cuda.synchronize()
+    d = _bits(out)
+    sentinel = _bits(torch.full((1,), float(SENTINEL_F32), dtype=torch.bfloat16))[0]
+    g = np.random.default_rng(403)
+    for e in range(16):
+        assert np.all(d[e, v[e]:] == sentinel)
+        if not v[e]:
+            continue
+        cols = g.choice(4096, 96, replace=False)
+        qa_o, ea_o = scaling.quantize_mx(a[e:e + 1, :v[e]])
+        qb_o, eb_o = scaling.quantize_mx(b[e:e + 1, cols])
+        C, S, F = ref_mx(qa_o[0], ea_o[0], qb_o[0], eb_o[0])
+        check_bf16(d[e, :v[e]][:, cols], C, S, 7168, f"mx full expert {e}", S_flush=F)
+
+
+def test_grouped_deterministic(dev):
+    v, a, b = _masked_inputs(6, 128, 384, 1024, workload=43)
+    qa, sa = scaling.quantize_1x128(a)
+    qb, sb = scaling.quantize_128x128(b)
+    ta, tsa, tb, tsb, tv = _gpu(qa, sa, qb, sb, v)
+    d1 = fg8.grouped_gemm_fp8_masked(ta, tsa, tb, tsb, tv, out_dtype=torch.float32)
+    d2 = fg8.grouped_gemm_fp8_masked(ta, tsa, tb, tsb, tv, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(d1.view(torch.int32), d2.view(torch.int32))
