@@ -21,8 +21,8 @@
 //     global_load_lds_dwordx4 / _dword (no staging registers), STAGES blocks
 //     in flight;
 //   * LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by
-//     (r & 7) ^ ((r >> 3) & 1), so the MFMA operand reads (ds_read_b128 of
-//     one chunk from 16 consecutive rows) hit distinct banks;
+//     (r >> 1) & 7, so the MFMA operand reads (ds_read_b128 of one chunk
+//     from 16 consecutive rows) hit distinct banks;
 //   * a persistent grid walks a linear list of work units: dense tiles
 //     (optionally split along K with a deterministic last-arriver reduction),
 //     contiguous-layout tiles whose expert comes from block_expert, or
@@ -43,7 +43,10 @@
 
 namespace fg8 {
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// 16-byte chunk swizzle of LDS row r.  Measured with SQ_LDS_BANK_CONFLICT on
+// gfx950: (r >> 1) & 7 leaves the MFMA operand reads (one chunk of 16
+// consecutive rows per ds_read_b128) free of bank conflicts.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 template <int BM_, int BN_, int WAVES_M_, int STAGES_, int OCC_>
 struct Cfg {
@@ -353,17 +356,26 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
 
     // ---- prologue: STAGES-1 K blocks in flight
     const int nkb = w.kb1 - w.kb0;
+    // The K blocks of a unit are walked starting at a unit-dependent offset:
+    // tiles that run at the same time and share an operand (the A rows of a
+    // skinny GEMM, the A tile of a row of output tiles) then read different
+    // K blocks of it instead of all hitting the same L2 lines at once.
+    const int rot = uniform(u % nkb);
+    auto kb_of = [&](int j) {
+      const int x = j + rot;
+      return w.kb0 + (x >= nkb ? x - nkb : x);
+    };
 #pragma unroll
     for (int s = 0; s < C::STAGES - 1; ++s)
-      if (s < nkb) issue_stage(w.kb0 + s, s);
+      if (s < nkb) issue_stage(kb_of(s), s);
 
     // ---- main loop
     for (int i = 0; i < nkb; ++i) {
-      const int kb = w.kb0 + i;
-      const int later = min(C::STAGES - 2, nkb - 1 - i);   // stages issued after kb
+      const int later = min(C::STAGES - 2, nkb - 1 - i);   // stages issued after this one
       wait_stages_after<LOADS, C::STAGES - 2>(later);
       __syncthreads();
-      if (i + C::STAGES - 1 < nkb) issue_stage(kb + C::STAGES - 1, (i + C::STAGES - 1) % C::STAGES);
+      if (i + C::STAGES - 1 < nkb)
+        issue_stage(kb_of(i + C::STAGES - 1), (i + C::STAGES - 1) % C::STAGES);
 
       if (wave_live) {
         const uint8_t* st = smem + (i % C::STAGES) * C::STAGE_BYTES;
@@ -399,18 +411,34 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
                 Ss + (wm0 + tm * 16 + 4 * (lane >> 4)) * 4);
             sc[tm] = v4f{s4.x * sbv, s4.y * sbv, s4.z * sbv, s4.w * sbv};
           }
+          // Two-level accumulation, software-pipelined: the MFMAs of column
+          // tile tn (one 128-K partial per 16x16 tile) are issued before the
+          // promotion FMAs of column tile tn-1, so the FP32 FMAs run while the
+          // matrix core works and no MFMA waits on the previous one's result.
+          v4f part[2][C::TM];
+          const v4f z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int tn = 0; tn < C::TN; ++tn) {
             const v8i fb = load_frag(Bs, wn0 + tn * 16, lane);
 #pragma unroll
-            for (int tm = 0; tm < C::TM; ++tm) {
-              const v4f z = {0.f, 0.f, 0.f, 0.f};
-              const v4f part =
+            for (int tm = 0; tm < C::TM; ++tm)
+              part[tn & 1][tm] =
                   __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[tm], fb, z, 0, 0, 0, 0, 0, 0);
+            if (tn > 0) {
 #pragma unroll
-              for (int v = 0; v < 4; ++v) acc[tm][tn][v] = fmaf(part[v], sc[tm][v], acc[tm][tn][v]);
+              for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                  acc[tm][tn - 1][v] =
+                      fmaf(part[(tn - 1) & 1][tm][v], sc[tm][v], acc[tm][tn - 1][v]);
             }
           }
+#pragma unroll
+          for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[tm][C::TN - 1][v] =
+                  fmaf(part[(C::TN - 1) & 1][tm][v], sc[tm][v], acc[tm][C::TN - 1][v]);
         }
       }
     }
@@ -537,10 +565,18 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
   TileChoice t{};
   int forced_splits = 0;
   bool forced = false;
-  if (p.mode == kContiguous) t.cfg = kCfgWide;
-  else if (p.mode == kDense && (forced = tile_override(&t.cfg, &forced_splits))) {}
-  else if (p.mode == kDense && p.M <= 64) t.cfg = kCfgS32;
-  else t.cfg = kCfgBig;
+  if (p.mode == kContiguous) {
+    t.cfg = kCfgWide;
+  } else if (p.mode == kDense && (forced = tile_override(&t.cfg, &forced_splits))) {
+  } else if (p.mode == kDense && p.M <= 64) {
+    // decode-sized M: narrow 64 x 32 tiles split along K, unless N alone
+    // gives two waves of them, then wider 64 x 128 tiles without a split
+    t.cfg = (p.N + 31) / 32 >= 2 * num_cus ? kCfgS128 : kCfgS32;
+  } else if (p.mode == kDense && p.M <= 128) {
+    t.cfg = kCfgM32;
+  } else {
+    t.cfg = kCfgBig;
+  }
   t.bm = kCfgs[t.cfg].bm;
   t.bn = kCfgs[t.cfg].bn;
   const int slots = num_cus * kCfgs[t.cfg].occ;

@@ -6,8 +6,8 @@
     32-element chunk, and the bias 127;
   * v_cvt_pk_fp8_f32: round-to-nearest-even, saturation and the sign of zero,
     compared with the oracle's encoder on a sweep through every e4m3 midpoint;
-  * e4m3 subnormal operands are flushed to zero by the FP8 MFMA (scaled and
-    unscaled), which the GEMM tolerance has to allow for;
+  * e4m3 subnormal operands times normal ones are used exactly by the FP8
+    MFMA (scaled and unscaled); products of two subnormals are reported;
   * how one MFMA rounds its 128-product sum (informational).
 Expected values come from the oracle's e4m3 table and the stated hypotheses.
 """
@@ -231,18 +231,28 @@ def _one_product(torch, lib, ca, cb, scaled=False):
 
 
 @pytest.mark.parametrize("scaled", [False, True])
-def test_mfma_flushes_e4m3_subnormal_inputs(env, scaled):
-    """An e4m3 subnormal operand (exponent field 0, mantissa != 0) contributes
-    nothing: the FP8 MFMA flushes it to zero, while the smallest normal 2^-6 is
-    used exactly.  The GEMM tolerance therefore carries the term
-    sum |a b| over products with a subnormal operand."""
+def test_mfma_keeps_e4m3_subnormal_inputs(env, scaled):
+    """An e4m3 subnormal operand (exponent field 0, mantissa m != 0, value
+    m * 2^-9) times a normal one contributes its exact product: the FP8 MFMA
+    does not flush it.  A product of two subnormals (m1 m2 2^-18) must come out
+    either exact or zero; which one is printed."""
     torch, lib = env
     assert _one_product(torch, lib, 0x08, 0x38, scaled) == 2.0 ** -6      # normal x 1
     assert _one_product(torch, lib, 0x88, 0x40, scaled) == -(2.0 ** -5)
     for sub in (0x01, 0x04, 0x07, 0x81):
-        got = _one_product(torch, lib, sub, 0x38, scaled)
-        assert got == 0.0, f"code {sub:#04x} x 1.0 gave {got!r}"
-        assert _one_product(torch, lib, 0x38, sub, scaled) == 0.0
+        val = e4m3.decode_code(sub)
+        for other, oval in ((0x38, 1.0), (0x48, 4.0), (0xB0, -0.5)):
+            got = _one_product(torch, lib, sub, other, scaled)
+            assert got == val * oval, f"code {sub:#04x} x {oval} gave {got!r}"
+            got = _one_product(torch, lib, other, sub, scaled)
+            assert got == val * oval, f"{oval} x code {sub:#04x} gave {got!r}"
+    seen = []
+    for ca, cb in ((0x01, 0x01), (0x07, 0x05), (0x84, 0x03)):
+        want = e4m3.decode_code(ca) * e4m3.decode_code(cb)
+        got = _one_product(torch, lib, ca, cb, scaled)
+        assert got in (want, 0.0), f"{ca:#04x} x {cb:#04x} gave {got!r}, exact {want!r}"
+        seen.append("exact" if got == want else "zero")
+    print(f"\nsubnormal x subnormal products (scaled={scaled}): {seen}")
 
 
 def test_mfma_internal_sum_informational(env):
@@ -261,6 +271,44 @@ def test_mfma_internal_sum_informational(env):
     exact = 126 * 2.0 ** -12
     print(f"\nMFMA chunk sum: got {got!r}, exact {exact!r}")
     assert abs(got - exact) <= 128 * 2.0 ** -24 * (2 * 448 * 448 + 126 * 2.0 ** -12)
+
+
+def _row0_dot(torch, lib, terms):
+    """D[0][0] of one 16x16x128 MFMA whose row 0 of A and column 0 of B hold
+    the given (k, code_a, code_b) terms and zeros elsewhere."""
+    A = np.zeros((16, 128), np.uint8)
+    B = np.zeros((16, 128), np.uint8)
+    for k, ca, cb in terms:
+        A[0, k], B[0, k] = ca, cb
+    return _unlanes16(_run_mfma(torch, lib, "probe_mfma16", _lanes16(A), _lanes16(B), 4))[0, 0]
+
+
+def test_mfma_alignment_informational(env):
+    """How far below the largest product of a 16-wide K group a small product
+    survives: +256 and -256 at K = 0, 1 cancel, and a third product x at K = 2
+    (same group) or K = 16 (next group) should come out as x.  Printed as a
+    table of log2(|x|) -> result / x for x = 2^-j and +-1.5 * 2^-j."""
+    torch, lib = env
+    enc = lambda v: int(e4m3.encode(float(v)))
+    big, nbig, one = enc(256.0), enc(-256.0), enc(1.0)
+    rows = []
+    for j in range(0, 19):
+        a, b = min(j, 9), j - min(j, 9)              # 2^-a (subnormal below 2^-6) times 2^-b
+        line = [f"2^-{j:<2d}"]
+        for mant, sign in ((1.0, 1), (1.5, 1), (1.5, -1)):
+            a2, b2 = (a, b) if mant == 1.0 else (min(j, 8), j - min(j, 8))
+            if b2 > 9:                               # 1.5 * 2^-j not a product of two codes
+                line.append(f"{'-':>8s} {'-':>8s}")
+                continue
+            ca, cb = enc(sign * mant * 2.0 ** -a2), enc(2.0 ** -b2)
+            want = sign * mant * 2.0 ** -j
+            assert e4m3.decode_code(ca) * e4m3.decode_code(cb) == want
+            same = _row0_dot(torch, lib, [(0, big, one), (1, nbig, one), (2, ca, cb)])
+            other = _row0_dot(torch, lib, [(0, big, one), (1, nbig, one), (16, ca, cb)])
+            line.append(f"{same / want:8.4f} {other / want:8.4f}")
+        rows.append(" | ".join(line))
+    print("\nx = 2^-j | (+1.0x) same-group next-group | (+1.5x) | (-1.5x), big products 2^8")
+    print("\n".join(rows))
 
 
 def test_copy_bandwidth_informational(env):
