@@ -36,6 +36,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "fg8_device.h"
 #include "fg8_internal.h"
 
@@ -134,21 +136,16 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int r0, int lane) 
   return f;
 }
 
-// Split-K partials are published with agent-scope relaxed atomic stores
-// (written through to the point of coherence shared by all XCDs) and read back
-// with agent-scope relaxed atomic loads; a vmcnt(0) wait orders them before
-// the arrival counter, so no L2 write-back fence is needed.
-__device__ __forceinline__ void store_coherent(float* p, v4f v) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __hip_atomic_store(p + i, v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ v4f load_coherent(const float* p) {
-  v4f v;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    v[i] = __hip_atomic_load(const_cast<float*>(p) + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return v;
+// Split-K partials are published with 16-byte buffer stores that carry the
+// agent-scope coherence bit (sc1: written through to the point of coherence
+// shared by all XCDs) and read back with sc1 buffer loads; a vmcnt(0) wait
+// orders them before the arrival counter, so no L2 write-back is needed.
+// Raw buffer descriptor: base, byte bound, no stride, gfx9 dword 3.
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kCoherent = 16;   // cache-policy operand of the buffer builtins: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferDword3);
 }
 __device__ __forceinline__ void wait_all_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -445,13 +442,16 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
 
     // ---- split-K: deterministic last-arriver reduction through the workspace
     if (MODE == kDense && splits > 1) {
-      float* part = p.ws_partial + ((int64_t)w.tile * splits + w.split) * (C::BM * C::BN);
+      constexpr uint32_t kTileBytes = C::BM * C::BN * 4;
+      const __amdgpu_buffer_rsrc_t ws =
+          buffer_rsrc(p.ws_partial + (int64_t)w.tile * splits * (C::BM * C::BN), kTileBytes * splits);
 #pragma unroll
       for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < C::TN; ++tn) {
-          const int idx = ((wave * C::TM + tm) * C::TN + tn) * 64 + lane;
-          store_coherent(part + 4 * idx, acc[tm][tn]);
+          const uint32_t idx = ((wave * C::TM + tm) * C::TN + tn) * 64 + lane;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, acc[tm][tn]), ws,
+                                                 w.split * kTileBytes + idx * 16, 0, kCoherent);
         }
       wait_all_memory();        // this thread's partials have reached the coherence point
       __syncthreads();          // ... and every other thread's
@@ -460,44 +460,70 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
                                       __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
       __syncthreads();
       if (!flag) continue;
-      const float* base = p.ws_partial + (int64_t)w.tile * splits * (C::BM * C::BN);
 #pragma unroll
       for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
         for (int tn = 0; tn < C::TN; ++tn) {
-          const int idx = ((wave * C::TM + tm) * C::TN + tn) * 64 + lane;
+          const uint32_t idx = ((wave * C::TM + tm) * C::TN + tn) * 64 + lane;
           v4f sum = {0.f, 0.f, 0.f, 0.f};
           for (int s = 0; s < splits; ++s)   // fixed order: bitwise reproducible
-            sum += s == w.split ? acc[tm][tn] : load_coherent(base + s * (C::BM * C::BN) + 4 * idx);
+            sum += s == w.split ? acc[tm][tn]
+                                : __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              ws, s * kTileBytes + idx * 16, 0,
+                                                              kCoherent));
           acc[tm][tn] = sum;
         }
       if (tid == 0)
         __hip_atomic_store(p.ws_counters + w.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // ---- epilogue: FP32 or BF16 (RNE), rows past the live count and columns
-    // past N are not written
-    if (wave_live) {
-      const int64_t d_off = MODE == kMasked ? (int64_t)w.g * M * N : 0;
+    // ---- epilogue: the tile is staged in LDS in the output type so that the
+    // global stores are 16-byte pieces of rows; FP32 or BF16 (RNE); rows past
+    // the live count and columns past N are not written.
+    __syncthreads();   // every wave is done with the stage buffers
+    auto store_tile = [&](auto esz_c) {
+      constexpr int ESZ = decltype(esz_c)::value;
+      constexpr int ROW = C::BN * ESZ + 16;   // padded LDS row: conflict-free writes
+      constexpr int CHUNKS = C::BN * ESZ / 16, PER = 16 / ESZ;
+      static_assert(C::BM * ROW <= C::STAGES * C::STAGE_BYTES, "output tile must fit in LDS");
+      if (wave_live) {
 #pragma unroll
-      for (int tm = 0; tm < C::TM; ++tm) {
+        for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
-        for (int tn = 0; tn < C::TN; ++tn) {
-          const int64_t col = w.n0 + wn0 + tn * 16 + (lane & 15);
+          for (int tn = 0; tn < C::TN; ++tn)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int64_t row = w.m0 + wm0 + tm * 16 + 4 * (lane >> 4) + v;
-            if (row < w.rows && col < N) {
-              const int64_t o = d_off + row * N + col;
-              if (p.out_bf16)
-                reinterpret_cast<uint16_t*>(p.d)[o] = f32_to_bf16(acc[tm][tn][v]);
+            for (int v = 0; v < 4; ++v) {
+              uint8_t* q = smem + (wm0 + tm * 16 + 4 * (lane >> 4) + v) * ROW +
+                           (wn0 + tn * 16 + (lane & 15)) * ESZ;
+              if constexpr (ESZ == 2)
+                *reinterpret_cast<uint16_t*>(q) = f32_to_bf16(acc[tm][tn][v]);
               else
-                reinterpret_cast<float*>(p.d)[o] = acc[tm][tn][v];
+                *reinterpret_cast<float*>(q) = acc[tm][tn][v];
             }
+      }
+      __syncthreads();
+      const int64_t d_off = MODE == kMasked ? (int64_t)w.g * M * N : 0;
+      const bool vec = (N * ESZ) % 16 == 0;   // every row starts 16-byte aligned
+      const int64_t live = min((int64_t)C::BM, (int64_t)w.rows - w.m0);
+      for (int idx = tid; idx < live * CHUNKS; idx += 256) {
+        const int r = idx / CHUNKS, ch = idx % CHUNKS;
+        const int64_t col = w.n0 + ch * PER;
+        const uint8_t* src = smem + r * ROW + ch * 16;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(p.d) + (d_off + (w.m0 + r) * N + col) * ESZ;
+        if (vec && col + PER <= N) {
+          *reinterpret_cast<int4*>(dst) = *reinterpret_cast<const int4*>(src);
+        } else {
+          for (int e = 0; e < PER && col + e < N; ++e) {
+            if constexpr (ESZ == 2)
+              reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+            else
+              reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src)[e];
           }
         }
       }
-    }
+    };
+    if (p.out_bf16) store_tile(std::integral_constant<int, 2>{});
+    else store_tile(std::integral_constant<int, 4>{});
   }
 }
 
