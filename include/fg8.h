@@ -44,8 +44,10 @@
  *     FG8_EUNSUPPORTED nothing was launched.  fg8_last_error() gives the text
  *     for the calling thread's last failure.  Faults inside a kernel surface
  *     at the caller's next synchronization.
- *   - Device-side index data (block_expert, valid_rows) is trusted: values out
- *     of range are undefined behaviour.
+ *   - Device-side index data is range-checked by the kernels: a 128-row
+ *     block whose block_expert value lies outside [0, E) is skipped (its
+ *     output rows are left as they were), and valid_rows values are clamped
+ *     to [0, cap] (gemm_mxfp8: [0, m]).
  *   - Calls may run concurrently on different streams; a split-K workspace
  *     must not be shared by calls that can overlap.
  *   - FP32 inputs to fp8_quantize must be finite.
@@ -124,7 +126,8 @@ size_t fg8_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
  * multiple of 128 rows; block_expert names the expert of every 128-row block.
  *   a  uint8 [m_total][k]         sa float [k/128][m_total]
  *   b  uint8 [E][n][k]            sb float [E][ceil(n/128)][k/128]
- *   block_expert int32 [m_total/128], values in [0, E)  (device memory)
+ *   block_expert int32 [m_total/128], values in [0, E); others skip the block
+ *                (device memory)
  *   d  [m_total][n] float or bfloat16 bits.  Every row is written, padding
  *   rows included (they are zero when the padding rows of a are zero).
  *   m_total % 128 == 0, k % 128 == 0 (else FG8_EUNSUPPORTED); E = num_experts >= 1.

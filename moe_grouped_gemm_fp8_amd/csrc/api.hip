@@ -38,8 +38,19 @@ fg8_status check_k(const char* fn, int64_t k) {
   return FG8_OK;
 }
 
+// The kernels count work units (tiles times splits) in 32-bit integers.
+fg8_status check_units(const fg8::GemmProblem& p, const fg8::TileChoice& t, const char* fn) {
+  const int64_t units = (int64_t)(p.mode == fg8::kMasked ? p.groups : 1) *
+                        ((p.M + t.bm - 1) / t.bm) * ((p.N + t.bn - 1) / t.bn) * t.splits;
+  if (units >= INT32_MAX)
+    return fail(FG8_EUNSUPPORTED, "%s: %lld tiles exceed the 32-bit work-unit count", fn,
+                (long long)units);
+  return FG8_OK;
+}
+
 fg8_status run(fg8::GemmProblem& p, const char* fn, hipStream_t stream) {
   const fg8::TileChoice t = fg8::choose_tiles(p, fg8::device_cu_count());
+  if (fg8_status st = check_units(p, t, fn)) return st;
   const hipError_t e = fg8::launch_gemm(p, t, stream);
   if (e != hipSuccess) return fail(FG8_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   g_err[0] = 0;
@@ -103,6 +114,7 @@ fg8_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t
   p.out_bf16 = out == FG8_OUT_BF16;
   p.mode = fg8::kDense; p.M = m; p.N = n; p.K = k; p.groups = 1;
   const fg8::TileChoice t = fg8::choose_tiles(p, fg8::device_cu_count());
+  if (fg8_status st = check_units(p, t, fn)) return st;
   if (t.splits > 1) {
     const size_t need = fg8::splitk_workspace_bytes(m, n, k, fg8::device_cu_count());
     if (!workspace || workspace_bytes < need)

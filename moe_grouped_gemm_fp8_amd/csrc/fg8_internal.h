@@ -24,6 +24,7 @@ struct GemmProblem {
   int groups;                   // experts (masked / contiguous) or 1
   const int32_t* block_expert;  // contiguous: expert of each 128-row block
   const int32_t* valid;         // masked: live rows per group (NULL = all M)
+  int rotate;                   // 1: start each unit's K walk at a unit-dependent block
   // split-K (dense only)
   int splits;
   float* ws_partial;
@@ -43,6 +44,7 @@ struct TileChoice {
   int bm, bn;
   int splits;
   int grid;
+  int rotate;
 };
 
 TileChoice choose_tiles(const GemmProblem& p, int num_cus);

@@ -50,23 +50,27 @@ namespace fg8 {
 // consecutive rows per ds_read_b128) free of bank conflicts.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-template <int BM_, int BN_, int WAVES_M_, int STAGES_, int OCC_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_>
 struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = 4 / WAVES_M_;
+  static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
   static constexpr int STAGES = STAGES_, OCC = OCC_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
   // One stage: A tile | B tile | A row scales (FP32 sa or E8M0 dwords) |
   // B row scales (E8M0 dwords, MX only) | one B-block scale per wave (FP32).
   static constexpr int A_BYTES = BM * kGroup, B_BYTES = BN * kGroup;
-  static constexpr int SA_BYTES = BM * 4, SB_BYTES = BN * 4, SBW_BYTES = 16;
+  static constexpr int SA_BYTES = BM * 4, SB_BYTES = BN * 4, SBW_BYTES = 4 * WAVES;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES + SBW_BYTES;
-  static constexpr int A_LOADS = BM / 32;   // 16-byte LDS-DMA loads per wave per stage
-  static constexpr int B_LOADS = BN / 32;
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile sides must be multiples of 32");
+  // rows each wave copies per stage; one 16-byte LDS-DMA load covers 8 rows
+  static constexpr int A_ROWS = BM / WAVES, B_ROWS = BN / WAVES;
+  static constexpr int A_LOADS = A_ROWS / 8, B_LOADS = B_ROWS / 8;
+  static_assert(A_ROWS % 8 == 0 && B_ROWS % 8 == 0, "every wave copies whole groups of 8 rows");
+  static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
   static_assert(WN <= 128 && (128 % WN) == 0, "a wave's columns must sit in one 128-block");
-  static_assert(BM / 4 <= 64 && BN / 4 <= 64, "one scale load per wave must cover its rows");
+  static_assert(A_ROWS <= 64 && B_ROWS <= 64, "one scale load per wave must cover its rows");
+  static_assert((STAGE_BYTES - SBW_BYTES) % 16 == 0 && SBW_BYTES % 16 == 0, "aligned stage parts");
   static_assert(STAGES >= 2, "need at least double buffering");
   static_assert(STAGE_BYTES % 16 == 0, "stages stay 16-byte aligned");
 };
@@ -158,7 +162,7 @@ struct Unit {
 };
 
 template <class C, bool MX, int MODE>
-__global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
+__global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGES * C::STAGE_BYTES];
   __shared__ int tile_prefix[MODE == kMasked ? 1025 : 1];
   __shared__ int flag;
@@ -177,14 +181,15 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
   if constexpr (MODE == kMasked) {
     // tiles per group from the device-side counts; exclusive prefix in LDS.
     const int G = p.groups;
-    int local[4];
+    constexpr int PER = 1024 / C::THREADS;   // groups per thread (G <= 1024)
+    int local[PER];
     int sum = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = tid * 4 + j;
+    for (int j = 0; j < PER; ++j) {
+      const int e = tid * PER + j;
       int v = 0;
       if (e < G) {
-        const int64_t rows = p.valid ? (int64_t)p.valid[e] : M;
+        const int64_t rows = p.valid ? min(max((int64_t)p.valid[e], (int64_t)0), M) : M;
         v = (int)((rows + C::BM - 1) / C::BM) * n_tiles;
       }
       local[j] = v;
@@ -197,19 +202,19 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
       const int t = __shfl_up(incl, o, 64);
       if (lane >= o) incl += t;
     }
-    __shared__ int wave_tot[4];
+    __shared__ int wave_tot[C::WAVES];
     if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
     int base = 0;
     for (int w = 0; w < wave; ++w) base += wave_tot[w];
     int run = base + incl - sum;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = tid * 4 + j;
+    for (int j = 0; j < PER; ++j) {
+      const int e = tid * PER + j;
       if (e < G) tile_prefix[e] = run;
       run += local[j];
     }
-    if (tid == 255) tile_prefix[G] = run;   // grand total (G <= 1024)
+    if (tid == C::THREADS - 1) tile_prefix[G] = run;   // grand total (G <= 1024)
     __syncthreads();
     total = tile_prefix[G];
   } else {
@@ -233,7 +238,7 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
       w.m0 = (int64_t)(t / n_tiles) * C::BM;
       w.n0 = (int64_t)(t % n_tiles) * C::BN;
       w.kb0 = 0; w.kb1 = KB; w.split = 0; w.tile = u;
-      w.rows = p.valid ? p.valid[lo] : (int)M;
+      w.rows = p.valid ? (int)min(max((int64_t)p.valid[lo], (int64_t)0), M) : (int)M;
     } else {
       const int t = u / splits;
       w.split = u % splits;
@@ -252,6 +257,8 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
     w.kb0 = uniform(w.kb0);
     w.kb1 = uniform(w.kb1);
     w.rows = uniform(w.rows);
+    // a 128-row block whose expert id is out of range is skipped (not written)
+    if (MODE == kContiguous && (w.g < 0 || w.g >= p.groups)) continue;
 
     const uint8_t* ga;
     const uint8_t* gb = p.b;
@@ -288,23 +295,23 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
     uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
-      const int r = wave * (C::BM / 4) + i * 8 + (lane >> 3);
+      const int r = wave * C::A_ROWS + i * 8 + (lane >> 3);
       const int64_t gr = w.m0 + r < last_row ? w.m0 + r : last_row;
       a_off[i] = (uint32_t)((gr - w.m0) * K + (((lane & 7) ^ swz(r)) << 4));
     }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
-      const int r = wave * (C::BN / 4) + i * 8 + (lane >> 3);
+      const int r = wave * C::B_ROWS + i * 8 + (lane >> 3);
       const int64_t gr = w.n0 + r < N - 1 ? w.n0 + r : N - 1;
       b_off[i] = (uint32_t)((gr - w.n0) * K + (((lane & 7) ^ swz(r)) << 4));
     }
     uint32_t sa_off, sb_off = 0;
     {
-      const int64_t r = w.m0 + wave * (C::BM / 4) + lane;
+      const int64_t r = w.m0 + wave * C::A_ROWS + lane;
       const int64_t gr = r < last_row ? r : last_row;
       sa_off = (uint32_t)((gr - w.m0) * (MX ? K / kMxBlock : 4));
       if constexpr (MX) {
-        const int64_t rb = w.n0 + wave * (C::BN / 4) + lane;
+        const int64_t rb = w.n0 + wave * C::B_ROWS + lane;
         sb_off = (uint32_t)(((rb < N - 1 ? rb : N - 1) - w.n0) * (K / kMxBlock));
       }
     }
@@ -320,24 +327,24 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
       const uint8_t* bb = uniform(b_tile + (int64_t)kb * kGroup);
 #pragma unroll
       for (int i = 0; i < C::A_LOADS; ++i)
-        dma16(ab, a_off[i], uniform(st + (uint32_t)((wave * (C::BM / 4) + i * 8) * kGroup)));
+        dma16(ab, a_off[i], uniform(st + (uint32_t)((wave * C::A_ROWS + i * 8) * kGroup)));
 #pragma unroll
       for (int i = 0; i < C::B_LOADS; ++i)
         dma16(bb, b_off[i],
-              uniform(st + (uint32_t)(C::A_BYTES + (wave * (C::BN / 4) + i * 8) * kGroup)));
+              uniform(st + (uint32_t)(C::A_BYTES + (wave * C::B_ROWS + i * 8) * kGroup)));
       const uint32_t sst = st + C::A_BYTES + C::B_BYTES;
       if constexpr (MX) {
         // E8M0 bytes of K block kb for each tile row: one dword per row.
         const uint8_t* eab = uniform(gea + w.m0 * (K / kMxBlock) + kb * 4);
         const uint8_t* ebb = uniform(geb + w.n0 * (K / kMxBlock) + kb * 4);
-        const uint32_t la = uniform(sst + (uint32_t)(wave * (C::BM / 4) * 4));
-        const uint32_t lb = uniform(sst + (uint32_t)(C::SA_BYTES + wave * (C::BN / 4) * 4));
-        if (lane < C::BM / 4) dma4(eab, sa_off, la);
-        if (lane < C::BN / 4) dma4(ebb, sb_off, lb);
+        const uint32_t la = uniform(sst + (uint32_t)(wave * C::A_ROWS * 4));
+        const uint32_t lb = uniform(sst + (uint32_t)(C::SA_BYTES + wave * C::B_ROWS * 4));
+        if (lane < C::A_ROWS) dma4(eab, sa_off, la);
+        if (lane < C::B_ROWS) dma4(ebb, sb_off, lb);
       } else {
         const float* sab = uniform(gsa + (int64_t)kb * M + w.m0);
-        const uint32_t la = uniform(sst + (uint32_t)(wave * (C::BM / 4) * 4));
-        if (lane < C::BM / 4) dma4(sab, sa_off, la);
+        const uint32_t la = uniform(sst + (uint32_t)(wave * C::A_ROWS * 4));
+        if (lane < C::A_ROWS) dma4(sab, sa_off, la);
         // this wave's B-block scale for K block kb, one lane
         const float* sbp = uniform(sb_row + kb);
         const uint32_t lw = uniform(sst + (uint32_t)(C::SA_BYTES + C::SB_BYTES + wave * 4));
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
     // tiles that run at the same time and share an operand (the A rows of a
     // skinny GEMM, the A tile of a row of output tiles) then read different
     // K blocks of it instead of all hitting the same L2 lines at once.
-    const int rot = uniform(u % nkb);
+    const int rot = p.rotate ? uniform(u % nkb) : 0;
     auto kb_of = [&](int j) {
       const int x = j + rot;
       return w.kb0 + (x >= nkb ? x - nkb : x);
@@ -411,16 +418,19 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
           // Two-level accumulation, software-pipelined: the MFMAs of column
           // tile tn (one 128-K partial per 16x16 tile) are issued before the
           // promotion FMAs of column tile tn-1, so the FP32 FMAs run while the
-          // matrix core works and no MFMA waits on the previous one's result.
+          // matrix core works and no MFMA waits on the previous one's result;
+          // the B fragment of column tile tn+1 is read from LDS meanwhile.
           v4f part[2][C::TM];
+          v8i fb[2];
           const v4f z = {0.f, 0.f, 0.f, 0.f};
+          fb[0] = load_frag(Bs, wn0, lane);
 #pragma unroll
           for (int tn = 0; tn < C::TN; ++tn) {
-            const v8i fb = load_frag(Bs, wn0 + tn * 16, lane);
+            if (tn + 1 < C::TN) fb[(tn + 1) & 1] = load_frag(Bs, wn0 + (tn + 1) * 16, lane);
 #pragma unroll
             for (int tm = 0; tm < C::TM; ++tm)
-              part[tn & 1][tm] =
-                  __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[tm], fb, z, 0, 0, 0, 0, 0, 0);
+              part[tn & 1][tm] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  fa[tm], fb[tn & 1], z, 0, 0, 0, 0, 0, 0);
             if (tn > 0) {
 #pragma unroll
               for (int tm = 0; tm < C::TM; ++tm)
@@ -428,6 +438,14 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
                 for (int v = 0; v < 4; ++v)
                   acc[tm][tn - 1][v] =
                       fmaf(part[(tn - 1) & 1][tm][v], sc[tm][v], acc[tm][tn - 1][v]);
+            }
+            // issue order: one MFMA, then the four promotion FMAs of the
+            // previous column tile's same row tile, the next B read early
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              if (tm == 0 && tn + 1 < C::TN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+              if (tn > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
             }
           }
 #pragma unroll
@@ -505,7 +523,7 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
       const int64_t d_off = MODE == kMasked ? (int64_t)w.g * M * N : 0;
       const bool vec = (N * ESZ) % 16 == 0;   // every row starts 16-byte aligned
       const int64_t live = min((int64_t)C::BM, (int64_t)w.rows - w.m0);
-      for (int idx = tid; idx < live * CHUNKS; idx += 256) {
+      for (int idx = tid; idx < live * CHUNKS; idx += C::THREADS) {
         const int r = idx / CHUNKS, ch = idx % CHUNKS;
         const int64_t col = w.n0 + ch * PER;
         const uint8_t* src = smem + r * ROW + ch * 16;
@@ -528,27 +546,31 @@ __global__ __launch_bounds__(256, C::OCC) void gemm_kernel(GemmProblem p) {
 }
 
 // ------------------------------------------------------------------ configs
-// Name                         BM   BN WAVES_M STAGES OCC      wave tile
-using CfgBig = Cfg<256, 128, 4, 3, 1>;       // 64 x 128
-using CfgWide = Cfg<128, 256, 2, 3, 1>;      // 64 x 128 (contiguous needs BM <= 128)
-using CfgS32 = Cfg<64, 32, 2, 8, 1>;         // 32 x 16, deep pipeline
-using CfgS32x2 = Cfg<64, 32, 2, 5, 2>;       // 32 x 16, two workgroups per CU
-using CfgS64 = Cfg<64, 64, 1, 6, 1>;         // 64 x 16
-using CfgS128 = Cfg<64, 128, 1, 5, 1>;       // 64 x 32
-using CfgM64 = Cfg<128, 64, 2, 5, 1>;        // 64 x 32
-using CfgM32 = Cfg<128, 32, 4, 6, 1>;        // 32 x 32
+// Name                     BM   BN  WAVES  STAGES OCC     wave tile
+using CfgBig = Cfg<256, 128, 4, 1, 3, 1>;    // 64 x 128
+using CfgWide = Cfg<128, 256, 2, 2, 3, 1>;   // 64 x 128 (contiguous needs BM <= 128)
+using CfgS32 = Cfg<64, 32, 2, 2, 8, 1>;      // 32 x 16, deep pipeline
+using CfgS32x2 = Cfg<64, 32, 2, 2, 5, 2>;    // 32 x 16, two workgroups per CU
+using CfgS64 = Cfg<64, 64, 1, 4, 6, 1>;      // 64 x 16
+using CfgS128 = Cfg<64, 128, 1, 4, 5, 1>;    // 64 x 32
+using CfgM64 = Cfg<128, 64, 2, 2, 5, 1>;     // 64 x 32
+using CfgM32 = Cfg<128, 32, 4, 1, 6, 1>;     // 32 x 32
+using CfgBig8 = Cfg<256, 128, 4, 2, 3, 1>;   // 64 x 64, two waves per SIMD
+using CfgWide8 = Cfg<128, 256, 2, 4, 3, 1>;  // 64 x 64, two waves per SIMD
 
 struct CfgInfo {
   int bm, bn, occ;
 };
+#define FG8_CFG_INFO(C) {C::BM, C::BN, C::OCC}
 static const CfgInfo kCfgs[] = {
-    {CfgBig::BM, CfgBig::BN, CfgBig::OCC},       {CfgWide::BM, CfgWide::BN, CfgWide::OCC},
-    {CfgS32::BM, CfgS32::BN, CfgS32::OCC},       {CfgS32x2::BM, CfgS32x2::BN, CfgS32x2::OCC},
-    {CfgS64::BM, CfgS64::BN, CfgS64::OCC},       {CfgS128::BM, CfgS128::BN, CfgS128::OCC},
-    {CfgM64::BM, CfgM64::BN, CfgM64::OCC},       {CfgM32::BM, CfgM32::BN, CfgM32::OCC},
+    FG8_CFG_INFO(CfgBig),  FG8_CFG_INFO(CfgWide), FG8_CFG_INFO(CfgS32),  FG8_CFG_INFO(CfgS32x2),
+    FG8_CFG_INFO(CfgS64),  FG8_CFG_INFO(CfgS128), FG8_CFG_INFO(CfgM64),  FG8_CFG_INFO(CfgM32),
+    FG8_CFG_INFO(CfgBig8), FG8_CFG_INFO(CfgWide8),
 };
+#undef FG8_CFG_INFO
 enum CfgId {
-  kCfgBig = 0, kCfgWide, kCfgS32, kCfgS32x2, kCfgS64, kCfgS128, kCfgM64, kCfgM32, kNumCfgs
+  kCfgBig = 0, kCfgWide, kCfgS32, kCfgS32x2, kCfgS64, kCfgS128, kCfgM64, kCfgM32, kCfgBig8,
+  kCfgWide8, kNumCfgs
 };
 
 int device_cu_count() {
@@ -576,7 +598,8 @@ static int dense_splits(int64_t tiles, int64_t kb, int slots) {
 }
 
 // FG8_TILE_OVERRIDE="cfg[,splits]" forces a compiled tile configuration (and
-// split count) for dense problems: a tuning hook, not needed for correctness.
+// split count): a tuning hook, not needed for correctness.  Grouped layouts
+// accept only the configurations compiled for them.
 static bool tile_override(int* cfg, int* splits) {
   const char* e = getenv("FG8_TILE_OVERRIDE");
   if (!e || !*e) return false;
@@ -591,8 +614,15 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
   TileChoice t{};
   int forced_splits = 0;
   bool forced = false;
-  if (p.mode == kContiguous) {
-    t.cfg = kCfgWide;
+  int ov = -1;
+  if (p.mode != kDense && tile_override(&ov, &forced_splits)) {
+    if (p.mode == kContiguous && (ov == kCfgWide || ov == kCfgWide8)) forced = true;
+    if (p.mode == kMasked && (ov == kCfgBig || ov == kCfgBig8)) forced = true;
+  }
+  if (forced) {
+    t.cfg = ov;
+  } else if (p.mode == kContiguous) {
+    t.cfg = kCfgWide8;
   } else if (p.mode == kDense && (forced = tile_override(&t.cfg, &forced_splits))) {
   } else if (p.mode == kDense && p.M <= 64) {
     // decode-sized M: narrow 64 x 32 tiles split along K, unless N alone
@@ -601,7 +631,7 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
   } else if (p.mode == kDense && p.M <= 128) {
     t.cfg = kCfgM32;
   } else {
-    t.cfg = kCfgBig;
+    t.cfg = kCfgBig8;
   }
   t.bm = kCfgs[t.cfg].bm;
   t.bn = kCfgs[t.cfg].bn;
@@ -623,6 +653,11 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
   }
   t.grid = (int)(units < slots ? units : slots);
   if (t.grid < 1) t.grid = 1;
+  // K rotation: measured to help the grouped layouts and large dense
+  // problems with short K, and to cost a little elsewhere (long K keeps the
+  // tiles of one XCD on the same K block, which the L2 then serves once).
+  t.rotate = p.mode != kDense || (p.M > 128 && p.K < 4096);
+  if (const char* e = getenv("FG8_ROTATE")) t.rotate = atoi(e) != 0;
   return t;
 }
 
@@ -637,12 +672,13 @@ size_t splitk_workspace_bytes(int64_t m, int64_t n, int64_t k, int num_cus) {
 
 template <class C, bool MX, int MODE>
 static hipError_t launch(const GemmProblem& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<C, MX, MODE>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<C, MX, MODE>), dim3(grid), dim3(C::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
   p.splits = t.splits;
+  p.rotate = t.rotate;
   switch (p.mode) {
     case kDense:
       switch (t.cfg) {
@@ -653,11 +689,18 @@ hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
         case kCfgS128: return launch<CfgS128, false, kDense>(p, t.grid, s);
         case kCfgM64: return launch<CfgM64, false, kDense>(p, t.grid, s);
         case kCfgM32: return launch<CfgM32, false, kDense>(p, t.grid, s);
+        case kCfgBig8: return launch<CfgBig8, false, kDense>(p, t.grid, s);
+        case kCfgWide8: return launch<CfgWide8, false, kDense>(p, t.grid, s);
         default: return launch<CfgBig, false, kDense>(p, t.grid, s);
       }
     case kContiguous:
+      if (t.cfg == kCfgWide8) return launch<CfgWide8, false, kContiguous>(p, t.grid, s);
       return launch<CfgWide, false, kContiguous>(p, t.grid, s);
     default:
+      if (t.cfg == kCfgBig8) {
+        if (p.mx) return launch<CfgBig8, true, kMasked>(p, t.grid, s);
+        return launch<CfgBig8, false, kMasked>(p, t.grid, s);
+      }
       if (p.mx) return launch<CfgBig, true, kMasked>(p, t.grid, s);
       return launch<CfgBig, false, kMasked>(p, t.grid, s);
   }

@@ -75,6 +75,35 @@ def test_contiguous_zero_expert_and_padding(dev):
     assert np.all(out[lay.row_token < 0] == 0)
 
 
+def test_contiguous_out_of_range_expert_ids_skip_their_block(dev):
+    """A 128-row block whose expert id lies outside [0, E) (here -1 and E) is
+    skipped: its output rows keep their previous contents; every other block
+    is computed as usual."""
+    c, (lay, a1, w1, a2, w2) = _small_contiguous(300, 512, 384, 6, 2)
+    qa, sa = scaling.quantize_1x128(a1)
+    qb, sb = scaling.quantize_128x128(w1)
+    C, S = gemm.grouped_contiguous(qa, sa, qb, sb, lay.block_expert)
+    be = lay.block_expert.copy()
+    bad = np.zeros(be.size, bool)
+    bad[0] = bad[-1] = True
+    be[0], be[-1] = -1, c.experts
+    ta, tsa, tb, tsb, tbe = _gpu(qa, sa, qb, sb, be)
+    out = torch.full((qa.shape[0], qb.shape[1]), float(SENTINEL_F32), dtype=torch.float32,
+                     device="cuda")
+    fg8.grouped_gemm_fp8_contiguous(ta, tsa, tb, tsb, tbe, out=out)
+    torch.cuda.synchronize()
+    d = out.cpu().numpy()
+    rows_bad = np.repeat(bad, 128)
+    assert np.all(d[rows_bad] == SENTINEL_F32)
+    good = ~rows_bad
+    F = np.zeros_like(C)
+    for e in range(c.experts):
+        rows = np.repeat((lay.block_expert == e) & ~bad, 128)
+        if rows.any():
+            F[rows] = ref_blockscaled(qa[rows], sa[:, rows], qb[e], sb[e])[2]
+    check_f32(d[good], C[good], S[good], c.hidden, "contiguous good blocks", S_flush=F[good])
+
+
 @pytest.mark.parametrize("which", ["w1", "w2"])
 def test_contiguous_full_size_sampled(dev, which):
     """The MoE workload at full size (8192 tokens, top-8 of 32 experts, Zipf
@@ -155,6 +184,28 @@ def test_masked_small(dev, out_dtype):
         if v[e]:
             F = ref_blockscaled(qa[e, :v[e]], sa[e][:, :v[e]], qb[e], sb[e])[2]
             _check(d[e, :v[e]], C[e, :v[e]], S[e, :v[e]], K, f"masked expert {e}", F=F)
+
+
+def test_masked_counts_are_clamped(dev):
+    """valid_rows entries below 0 act as 0 and entries above cap act as cap."""
+    E, cap, N, K = 3, 64, 96, 256
+    v_eff = np.array([0, 64, 10], np.int32)
+    _, a, b = _masked_inputs(E, cap, N, K, valid=v_eff)
+    qa, sa = scaling.quantize_1x128(a)
+    qb, sb = scaling.quantize_128x128(b)
+    C, S = gemm.grouped_masked(qa, sa, qb, sb, v_eff)
+    ta, tsa, tb, tsb = _gpu(qa, sa, qb, sb)
+    tv = torch.tensor([-5, 1000, 10], dtype=torch.int32, device="cuda")
+    out = torch.full((E, cap, N), float(SENTINEL_F32), dtype=torch.float32, device="cuda")
+    fg8.grouped_gemm_fp8_masked(ta, tsa, tb, tsb, tv, out=out)
+    torch.cuda.synchronize()
+    d = out.cpu().numpy()
+    for e in range(E):
+        assert np.all(d[e, v_eff[e]:] == SENTINEL_F32), f"expert {e}"
+        if v_eff[e]:
+            F = ref_blockscaled(qa[e, :v_eff[e]], sa[e][:, :v_eff[e]], qb[e], sb[e])[2]
+            check_f32(d[e, :v_eff[e]], C[e, :v_eff[e]], S[e, :v_eff[e]], K, f"clamped {e}",
+                      S_flush=F)
 
 
 def test_masked_full_size_sampled(dev):
