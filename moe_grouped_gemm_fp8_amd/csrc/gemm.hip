@@ -50,18 +50,25 @@ namespace fg8 {
 // consecutive rows per ds_read_b128) free of bank conflicts.
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_, int KS_ = 1,
+          bool SPREAD_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WAVES = WAVES_M * WAVES_N, THREADS = 64 * WAVES;
   static constexpr int STAGES = STAGES_, OCC = OCC_;
+  static constexpr int KS = KS_;   // 128-wide K blocks per pipeline stage (one barrier each)
+  // SPREAD: the next stage's loads are issued between the column tiles of the
+  // compute instead of all at once after the barrier
+  static constexpr bool SPREAD = SPREAD_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
-  // One stage: A tile | B tile | A row scales (FP32 sa or E8M0 dwords) |
-  // B row scales (E8M0 dwords, MX only) | one B-block scale per wave (FP32).
+  // One stage holds KS K blocks, each laid out as: A tile | B tile | A row
+  // scales (FP32 sa or E8M0 dwords) | B row scales (E8M0 dwords, MX only) |
+  // one B-block scale per wave (FP32).
   static constexpr int A_BYTES = BM * kGroup, B_BYTES = BN * kGroup;
   static constexpr int SA_BYTES = BM * 4, SB_BYTES = BN * 4, SBW_BYTES = 4 * WAVES;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES + SBW_BYTES;
+  static constexpr int BLOCK_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES + SBW_BYTES;
+  static constexpr int STAGE_BYTES = KS * BLOCK_BYTES;
   // rows each wave copies per stage; one 16-byte LDS-DMA load covers 8 rows
   static constexpr int A_ROWS = BM / WAVES, B_ROWS = BN / WAVES;
   static constexpr int A_LOADS = A_ROWS / 8, B_LOADS = B_ROWS / 8;
@@ -70,7 +77,7 @@ struct Cfg {
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
   static_assert(WN <= 128 && (128 % WN) == 0, "a wave's columns must sit in one 128-block");
   static_assert(A_ROWS <= 64 && B_ROWS <= 64, "one scale load per wave must cover its rows");
-  static_assert((STAGE_BYTES - SBW_BYTES) % 16 == 0 && SBW_BYTES % 16 == 0, "aligned stage parts");
+  static_assert((BLOCK_BYTES - SBW_BYTES) % 16 == 0 && SBW_BYTES % 16 == 0, "aligned stage parts");
   static_assert(STAGES >= 2, "need at least double buffering");
   static_assert(STAGE_BYTES % 16 == 0, "stages stay 16-byte aligned");
 };
@@ -321,37 +328,51 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
     const float* sb_row = MX ? nullptr : gsb + nbw * KB;
     const uint8_t* a_tile = ga + w.m0 * K;
     const uint8_t* b_tile = gb + w.n0 * K;
-    auto issue_stage = [&](int kb, int stage) {
-      const uint32_t st = uniform(lds0 + (uint32_t)(stage * C::STAGE_BYTES));
-      const uint8_t* ab = uniform(a_tile + (int64_t)kb * kGroup);
-      const uint8_t* bb = uniform(b_tile + (int64_t)kb * kGroup);
-#pragma unroll
-      for (int i = 0; i < C::A_LOADS; ++i)
-        dma16(ab, a_off[i], uniform(st + (uint32_t)((wave * C::A_ROWS + i * 8) * kGroup)));
-#pragma unroll
-      for (int i = 0; i < C::B_LOADS; ++i)
+    // One LDS-DMA instruction of K block kb into block slot `sub` of stage
+    // `stage`: r < A_LOADS copies 8 A rows, then B_LOADS copies of 8 B rows,
+    // then the A row scales and the B scales (one dword per row, or the
+    // wave's one B-block scale).
+    constexpr int PB = C::A_LOADS + C::B_LOADS + 2;   // loads per K block and wave
+    auto issue_part = [&](int kb, int stage, int sub, int r) {
+      const uint32_t st =
+          uniform(lds0 + (uint32_t)(stage * C::STAGE_BYTES + sub * C::BLOCK_BYTES));
+      const uint32_t sst = st + C::A_BYTES + C::B_BYTES;
+      if (r < C::A_LOADS) {
+        const uint8_t* ab = uniform(a_tile + (int64_t)kb * kGroup);
+        dma16(ab, a_off[r], uniform(st + (uint32_t)((wave * C::A_ROWS + r * 8) * kGroup)));
+      } else if (r < C::A_LOADS + C::B_LOADS) {
+        const int i = r - C::A_LOADS;
+        const uint8_t* bb = uniform(b_tile + (int64_t)kb * kGroup);
         dma16(bb, b_off[i],
               uniform(st + (uint32_t)(C::A_BYTES + (wave * C::B_ROWS + i * 8) * kGroup)));
-      const uint32_t sst = st + C::A_BYTES + C::B_BYTES;
-      if constexpr (MX) {
-        // E8M0 bytes of K block kb for each tile row: one dword per row.
-        const uint8_t* eab = uniform(gea + w.m0 * (K / kMxBlock) + kb * 4);
-        const uint8_t* ebb = uniform(geb + w.n0 * (K / kMxBlock) + kb * 4);
-        const uint32_t la = uniform(sst + (uint32_t)(wave * C::A_ROWS * 4));
-        const uint32_t lb = uniform(sst + (uint32_t)(C::SA_BYTES + wave * C::B_ROWS * 4));
-        if (lane < C::A_ROWS) dma4(eab, sa_off, la);
-        if (lane < C::B_ROWS) dma4(ebb, sb_off, lb);
+      } else if (r == C::A_LOADS + C::B_LOADS) {
+        if constexpr (MX) {
+          // E8M0 bytes of K block kb for each tile row: one dword per row
+          const uint8_t* eab = uniform(gea + w.m0 * (K / kMxBlock) + kb * 4);
+          const uint32_t la = uniform(sst + (uint32_t)(wave * C::A_ROWS * 4));
+          if (lane < C::A_ROWS) dma4(eab, sa_off, la);
+        } else {
+          const float* sab = uniform(gsa + (int64_t)kb * M + w.m0);
+          const uint32_t la = uniform(sst + (uint32_t)(wave * C::A_ROWS * 4));
+          if (lane < C::A_ROWS) dma4(sab, sa_off, la);
+        }
       } else {
-        const float* sab = uniform(gsa + (int64_t)kb * M + w.m0);
-        const uint32_t la = uniform(sst + (uint32_t)(wave * C::A_ROWS * 4));
-        if (lane < C::A_ROWS) dma4(sab, sa_off, la);
-        // this wave's B-block scale for K block kb, one lane
-        const float* sbp = uniform(sb_row + kb);
-        const uint32_t lw = uniform(sst + (uint32_t)(C::SA_BYTES + C::SB_BYTES + wave * 4));
-        if (lane == 0) dma4(sbp, 0u, lw);
+        if constexpr (MX) {
+          const uint8_t* ebb = uniform(geb + w.n0 * (K / kMxBlock) + kb * 4);
+          const uint32_t lb = uniform(sst + (uint32_t)(C::SA_BYTES + wave * C::B_ROWS * 4));
+          if (lane < C::B_ROWS) dma4(ebb, sb_off, lb);
+        } else {
+          // this wave's B-block scale for K block kb, one lane
+          const float* sbp = uniform(sb_row + kb);
+          const uint32_t lw = uniform(sst + (uint32_t)(C::SA_BYTES + C::SB_BYTES + wave * 4));
+          if (lane == 0) dma4(sbp, 0u, lw);
+        }
       }
     };
-    constexpr int LOADS = C::A_LOADS + C::B_LOADS + 2;
+    // loads per stage: every stage issues KS K blocks (past the end of the
+    // unit the last K block is fetched again and not used), so that the
+    // per-stage count is fixed
+    constexpr int LOADS = C::KS * PB;
 
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
@@ -369,26 +390,53 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       const int x = j + rot;
       return w.kb0 + (x >= nkb ? x - nkb : x);
     };
+    const int nst = (nkb + C::KS - 1) / C::KS;   // stages of this unit
+    auto issue_range = [&](int si, int stage, int p0, int p1) {
 #pragma unroll
+      for (int q = 0; q < LOADS; ++q)
+        if (q >= p0 && q < p1)
+          issue_part(kb_of(min(si * C::KS + q / PB, nkb - 1)), stage, q / PB, q % PB);
+    };
     for (int s = 0; s < C::STAGES - 1; ++s)
-      if (s < nkb) issue_stage(kb_of(s), s);
+      if (s < nst) issue_range(s, s, 0, LOADS);
 
-    // ---- main loop
-    for (int i = 0; i < nkb; ++i) {
-      const int later = min(C::STAGES - 2, nkb - 1 - i);   // stages issued after this one
+    // ---- main loop.  The loads of stage si + STAGES - 1 are spread over the
+    // compute of stage si (after the MFMAs of each column tile), so that a
+    // load instruction that waits for room in the memory pipeline holds up
+    // the wave while its MFMAs are already running.
+    constexpr int POINTS = C::KS * C::TN;
+    for (int si = 0; si < nst; ++si) {
+      const int later = min(C::STAGES - 2, nst - 1 - si);   // stages issued after this one
       wait_stages_after<LOADS, C::STAGES - 2>(later);
       __syncthreads();
-      if (i + C::STAGES - 1 < nkb)
-        issue_stage(kb_of(i + C::STAGES - 1), (i + C::STAGES - 1) % C::STAGES);
-
-      if (wave_live) {
-        const uint8_t* st = smem + (i % C::STAGES) * C::STAGE_BYTES;
+      const int nsi = si + C::STAGES - 1;
+      const bool more = nsi < nst;
+      const int nstage = nsi % C::STAGES;
+      auto issue_point = [&](int pt) {
+        if (C::SPREAD && more)
+          issue_range(nsi, nstage, pt * LOADS / POINTS, (pt + 1) * LOADS / POINTS);
+      };
+      if (!C::SPREAD || !wave_live) {
+        if (more) issue_range(nsi, nstage, 0, LOADS);
+        if (!wave_live) continue;
+      }
+#pragma unroll
+      for (int sub = 0; sub < C::KS; ++sub) {
+        const bool active = C::KS == 1 || si * C::KS + sub < nkb;
+        const uint8_t* st = smem + (si % C::STAGES) * C::STAGE_BYTES + sub * C::BLOCK_BYTES;
         const uint8_t* As = st;
         const uint8_t* Bs = st + C::A_BYTES;
         const uint8_t* Ss = st + C::A_BYTES + C::B_BYTES;
-        v8i fa[C::TM];
+        if (!active) {
 #pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm) fa[tm] = load_frag(As, wm0 + tm * 16, lane);
+          for (int tn = 0; tn < C::TN; ++tn) issue_point(sub * C::TN + tn);
+          continue;
+        }
+        v8i fa[C::TM];
+        fa[0] = load_frag(As, wm0, lane);
+        const v8i fb0 = load_frag(Bs, wn0, lane);   // the first MFMA needs only these two
+#pragma unroll
+        for (int tm = 1; tm < C::TM; ++tm) fa[tm] = load_frag(As, wm0 + tm * 16, lane);
         if constexpr (MX) {
           int sA[C::TM];
 #pragma unroll
@@ -397,13 +445,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
                            (8 * (lane >> 4)));
 #pragma unroll
           for (int tn = 0; tn < C::TN; ++tn) {
-            const v8i fb = load_frag(Bs, wn0 + tn * 16, lane);
+            const v8i fb = tn == 0 ? fb0 : load_frag(Bs, wn0 + tn * 16, lane);
             const int sB = (int)(reinterpret_cast<const uint32_t*>(Ss + C::SA_BYTES)
                                      [wn0 + tn * 16 + (lane & 15)] >> (8 * (lane >> 4)));
 #pragma unroll
             for (int tm = 0; tm < C::TM; ++tm)
               acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                   fa[tm], fb, acc[tm][tn], 0, 0, 0, sA[tm], 0, sB);
+            issue_point(sub * C::TN + tn);
           }
         } else {
           const float sbv =
@@ -423,7 +472,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
           v4f part[2][C::TM];
           v8i fb[2];
           const v4f z = {0.f, 0.f, 0.f, 0.f};
-          fb[0] = load_frag(Bs, wn0, lane);
+          fb[0] = fb0;
 #pragma unroll
           for (int tn = 0; tn < C::TN; ++tn) {
             if (tn + 1 < C::TN) fb[(tn + 1) & 1] = load_frag(Bs, wn0 + (tn + 1) * 16, lane);
@@ -439,14 +488,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
                   acc[tm][tn - 1][v] =
                       fmaf(part[(tn - 1) & 1][tm][v], sc[tm][v], acc[tm][tn - 1][v]);
             }
-            // issue order: one MFMA, then the four promotion FMAs of the
-            // previous column tile's same row tile, the next B read early
-#pragma unroll
-            for (int tm = 0; tm < C::TM; ++tm) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              if (tm == 0 && tn + 1 < C::TN) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-              if (tn > 0) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            }
+            issue_point(sub * C::TN + tn);
           }
 #pragma unroll
           for (int tm = 0; tm < C::TM; ++tm)
@@ -547,16 +589,23 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
 
 // ------------------------------------------------------------------ configs
 // Name                     BM   BN  WAVES  STAGES OCC     wave tile
-using CfgBig = Cfg<256, 128, 4, 1, 3, 1>;    // 64 x 128
-using CfgWide = Cfg<128, 256, 2, 2, 3, 1>;   // 64 x 128 (contiguous needs BM <= 128)
+using CfgBig = Cfg<256, 128, 4, 1, 3, 1, 1, true>;    // 64 x 128
+using CfgWide = Cfg<128, 256, 2, 2, 3, 1, 1, true>;   // 64 x 128 (contiguous needs BM <= 128)
 using CfgS32 = Cfg<64, 32, 2, 2, 8, 1>;      // 32 x 16, deep pipeline
 using CfgS32x2 = Cfg<64, 32, 2, 2, 5, 2>;    // 32 x 16, two workgroups per CU
 using CfgS64 = Cfg<64, 64, 1, 4, 6, 1>;      // 64 x 16
 using CfgS128 = Cfg<64, 128, 1, 4, 5, 1>;    // 64 x 32
 using CfgM64 = Cfg<128, 64, 2, 2, 5, 1>;     // 64 x 32
 using CfgM32 = Cfg<128, 32, 4, 1, 6, 1>;     // 32 x 32
-using CfgBig8 = Cfg<256, 128, 4, 2, 3, 1>;   // 64 x 64, two waves per SIMD
-using CfgWide8 = Cfg<128, 256, 2, 4, 3, 1>;  // 64 x 64, two waves per SIMD
+using CfgBig8 = Cfg<256, 128, 4, 2, 3, 1, 1, true>;   // 64 x 64, two waves per SIMD
+using CfgWide8 = Cfg<128, 256, 2, 4, 3, 1, 1, true>;  // 64 x 64, two waves per SIMD
+// several K blocks per stage (one barrier per stage): decode-sized M
+using CfgS32k4 = Cfg<64, 32, 2, 2, 3, 1, 4>;   // 32 x 16
+using CfgS32k2 = Cfg<64, 32, 2, 2, 5, 1, 2>;   // 32 x 16
+using CfgS64k4 = Cfg<64, 64, 1, 4, 2, 1, 4>;   // 64 x 16
+using CfgS64k2 = Cfg<64, 64, 1, 4, 4, 1, 2>;   // 64 x 16
+using CfgS128k2 = Cfg<64, 128, 1, 4, 3, 1, 2>; // 64 x 32
+using CfgM32k2 = Cfg<128, 32, 4, 1, 3, 1, 2>;  // 32 x 32
 
 struct CfgInfo {
   int bm, bn, occ;
@@ -565,12 +614,13 @@ struct CfgInfo {
 static const CfgInfo kCfgs[] = {
     FG8_CFG_INFO(CfgBig),  FG8_CFG_INFO(CfgWide), FG8_CFG_INFO(CfgS32),  FG8_CFG_INFO(CfgS32x2),
     FG8_CFG_INFO(CfgS64),  FG8_CFG_INFO(CfgS128), FG8_CFG_INFO(CfgM64),  FG8_CFG_INFO(CfgM32),
-    FG8_CFG_INFO(CfgBig8), FG8_CFG_INFO(CfgWide8),
+    FG8_CFG_INFO(CfgBig8), FG8_CFG_INFO(CfgWide8), FG8_CFG_INFO(CfgS32k4), FG8_CFG_INFO(CfgS32k2),
+    FG8_CFG_INFO(CfgS64k4), FG8_CFG_INFO(CfgS64k2), FG8_CFG_INFO(CfgS128k2), FG8_CFG_INFO(CfgM32k2),
 };
 #undef FG8_CFG_INFO
 enum CfgId {
   kCfgBig = 0, kCfgWide, kCfgS32, kCfgS32x2, kCfgS64, kCfgS128, kCfgM64, kCfgM32, kCfgBig8,
-  kCfgWide8, kNumCfgs
+  kCfgWide8, kCfgS32k4, kCfgS32k2, kCfgS64k4, kCfgS64k2, kCfgS128k2, kCfgM32k2, kNumCfgs
 };
 
 int device_cu_count() {
@@ -625,11 +675,12 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
     t.cfg = kCfgWide8;
   } else if (p.mode == kDense && (forced = tile_override(&t.cfg, &forced_splits))) {
   } else if (p.mode == kDense && p.M <= 64) {
-    // decode-sized M: narrow 64 x 32 tiles split along K, unless N alone
-    // gives two waves of them, then wider 64 x 128 tiles without a split
-    t.cfg = (p.N + 31) / 32 >= 2 * num_cus ? kCfgS128 : kCfgS32;
+    // decode-sized M: narrow 64 x 32 tiles (four K blocks per stage) split
+    // along K, unless N alone gives two waves of them, then wider 64 x 128
+    // tiles without a split
+    t.cfg = (p.N + 31) / 32 >= 2 * num_cus ? kCfgS128 : kCfgS32k4;
   } else if (p.mode == kDense && p.M <= 128) {
-    t.cfg = kCfgM32;
+    t.cfg = kCfgS64k2;
   } else {
     t.cfg = kCfgBig8;
   }
@@ -653,10 +704,10 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
   }
   t.grid = (int)(units < slots ? units : slots);
   if (t.grid < 1) t.grid = 1;
-  // K rotation: measured to help the grouped layouts and large dense
-  // problems with short K, and to cost a little elsewhere (long K keeps the
-  // tiles of one XCD on the same K block, which the L2 then serves once).
-  t.rotate = p.mode != kDense || (p.M > 128 && p.K < 4096);
+  // K rotation: off.  Measured on the dense and grouped workloads, tiles that
+  // walk K in step are faster: the tiles of one XCD then share the same K
+  // block of their common A or B rows, which the L2 serves once.
+  t.rotate = 0;
   if (const char* e = getenv("FG8_ROTATE")) t.rotate = atoi(e) != 0;
   return t;
 }
@@ -691,6 +742,12 @@ hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
         case kCfgM32: return launch<CfgM32, false, kDense>(p, t.grid, s);
         case kCfgBig8: return launch<CfgBig8, false, kDense>(p, t.grid, s);
         case kCfgWide8: return launch<CfgWide8, false, kDense>(p, t.grid, s);
+        case kCfgS32k4: return launch<CfgS32k4, false, kDense>(p, t.grid, s);
+        case kCfgS32k2: return launch<CfgS32k2, false, kDense>(p, t.grid, s);
+        case kCfgS64k4: return launch<CfgS64k4, false, kDense>(p, t.grid, s);
+        case kCfgS64k2: return launch<CfgS64k2, false, kDense>(p, t.grid, s);
+        case kCfgS128k2: return launch<CfgS128k2, false, kDense>(p, t.grid, s);
+        case kCfgM32k2: return launch<CfgM32k2, false, kDense>(p, t.grid, s);
         default: return launch<CfgBig, false, kDense>(p, t.grid, s);
       }
     case kContiguous:
