@@ -37,6 +37,7 @@ struct GemmProblem {
 // reused across shapes: every completed call leaves all counters at zero and
 // partial sums never land on them.
 constexpr int kSplitKMaxTiles = 1024;
+constexpr int kMaxSplits = 8;   // K splits per tile
 constexpr size_t kSplitKCounterBytes = kSplitKMaxTiles * sizeof(int32_t);
 
 struct TileChoice {

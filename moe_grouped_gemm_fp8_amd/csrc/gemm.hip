@@ -60,6 +60,9 @@ struct Cfg {
   // SPREAD: the next stage's loads are issued between the column tiles of the
   // compute instead of all at once after the barrier
   static constexpr bool SPREAD = SPREAD_;
+  // split-K is compiled only into the decode-sized configurations (the large
+  // tiles have no registers to spare for the partial sums)
+  static constexpr bool SPLITK = WAVES == 4 && BM <= 128 && BN <= 128;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
   // One stage holds KS K blocks, each laid out as: A tile | B tile | A row
@@ -501,7 +504,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
     }
 
     // ---- split-K: deterministic last-arriver reduction through the workspace
-    if (MODE == kDense && splits > 1) {
+    if (C::SPLITK && MODE == kDense && splits > 1) {
       constexpr uint32_t kTileBytes = C::BM * C::BN * 4;
       const __amdgpu_buffer_rsrc_t ws =
           buffer_rsrc(p.ws_partial + (int64_t)w.tile * splits * (C::BM * C::BN), kTileBytes * splits);
@@ -520,19 +523,38 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
                                       __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
       __syncthreads();
       if (!flag) continue;
+      // All partial loads of a batch of output tiles are issued before the
+      // first is used, so their latencies overlap; the sum runs in split
+      // order (bitwise reproducible).
+      constexpr int NT = C::TM * C::TN;
+      // (two-waves-per-SIMD tiles have no registers to spare: one tile at a time)
+      constexpr int BATCH = C::WAVES == 8 ? 1 : (NT < 4 ? NT : 4);
 #pragma unroll
-      for (int tm = 0; tm < C::TM; ++tm)
+      for (int t0 = 0; t0 < NT; t0 += BATCH) {
+        v4f part[BATCH][kMaxSplits];
 #pragma unroll
-        for (int tn = 0; tn < C::TN; ++tn) {
-          const uint32_t idx = ((wave * C::TM + tm) * C::TN + tn) * 64 + lane;
+        for (int b = 0; b < BATCH; ++b)
+#pragma unroll
+          for (int s = 0; s < kMaxSplits; ++s) {
+            const int t = t0 + b;
+            const uint32_t idx = (wave * NT + t) * 64 + lane;
+            if (t < NT && s < splits && s != w.split)
+              part[b][s] = __builtin_bit_cast(
+                  v4f, __builtin_amdgcn_raw_buffer_load_b128(ws, s * kTileBytes + idx * 16, 0,
+                                                             kCoherent));
+          }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+          const int t = t0 + b;
+          if (t >= NT) break;
+          v4f& a = acc[t / C::TN][t % C::TN];
           v4f sum = {0.f, 0.f, 0.f, 0.f};
-          for (int s = 0; s < splits; ++s)   // fixed order: bitwise reproducible
-            sum += s == w.split ? acc[tm][tn]
-                                : __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                                              ws, s * kTileBytes + idx * 16, 0,
-                                                              kCoherent));
-          acc[tm][tn] = sum;
+#pragma unroll
+          for (int s = 0; s < kMaxSplits; ++s)
+            if (s < splits) sum += s == w.split ? a : part[b][s];
+          a = sum;
         }
+      }
       if (tid == 0)
         __hip_atomic_store(p.ws_counters + w.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -545,39 +567,47 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       constexpr int ESZ = decltype(esz_c)::value;
       constexpr int ROW = C::BN * ESZ + 16;   // padded LDS row: conflict-free writes
       constexpr int CHUNKS = C::BN * ESZ / 16, PER = 16 / ESZ;
-      static_assert(C::BM * ROW <= C::STAGES * C::STAGE_BYTES, "output tile must fit in LDS");
-      if (wave_live) {
-#pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm)
-#pragma unroll
-          for (int tn = 0; tn < C::TN; ++tn)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              uint8_t* q = smem + (wm0 + tm * 16 + 4 * (lane >> 4) + v) * ROW +
-                           (wn0 + tn * 16 + (lane & 15)) * ESZ;
-              if constexpr (ESZ == 2)
-                *reinterpret_cast<uint16_t*>(q) = f32_to_bf16(acc[tm][tn][v]);
-              else
-                *reinterpret_cast<float*>(q) = acc[tm][tn][v];
-            }
-      }
-      __syncthreads();
+      // rows staged at a time: whole wave row blocks that fit in the stage memory
+      constexpr int FIT = C::STAGES * C::STAGE_BYTES / ROW;
+      constexpr int CR = FIT >= C::BM ? C::BM : (FIT / C::WM) * C::WM;
+      static_assert(CR >= C::WM && C::BM % CR == 0, "output rows must stage in whole wave blocks");
       const int64_t d_off = MODE == kMasked ? (int64_t)w.g * M * N : 0;
       const bool vec = (N * ESZ) % 16 == 0;   // every row starts 16-byte aligned
-      const int64_t live = min((int64_t)C::BM, (int64_t)w.rows - w.m0);
-      for (int idx = tid; idx < live * CHUNKS; idx += C::THREADS) {
-        const int r = idx / CHUNKS, ch = idx % CHUNKS;
-        const int64_t col = w.n0 + ch * PER;
-        const uint8_t* src = smem + r * ROW + ch * 16;
-        uint8_t* dst = reinterpret_cast<uint8_t*>(p.d) + (d_off + (w.m0 + r) * N + col) * ESZ;
-        if (vec && col + PER <= N) {
-          *reinterpret_cast<int4*>(dst) = *reinterpret_cast<const int4*>(src);
-        } else {
-          for (int e = 0; e < PER && col + e < N; ++e) {
-            if constexpr (ESZ == 2)
-              reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
-            else
-              reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src)[e];
+#pragma unroll
+      for (int r0 = 0; r0 < C::BM; r0 += CR) {
+        if (r0 > 0) __syncthreads();   // the previous rows have left LDS
+        if (wave_live && wm0 >= r0 && wm0 < r0 + CR) {
+#pragma unroll
+          for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                uint8_t* q = smem + (wm0 - r0 + tm * 16 + 4 * (lane >> 4) + v) * ROW +
+                             (wn0 + tn * 16 + (lane & 15)) * ESZ;
+                if constexpr (ESZ == 2)
+                  *reinterpret_cast<uint16_t*>(q) = f32_to_bf16(acc[tm][tn][v]);
+                else
+                  *reinterpret_cast<float*>(q) = acc[tm][tn][v];
+              }
+        }
+        __syncthreads();
+        const int64_t live = min((int64_t)CR, (int64_t)w.rows - w.m0 - r0);
+        for (int idx = tid; idx < live * CHUNKS; idx += C::THREADS) {
+          const int r = idx / CHUNKS, ch = idx % CHUNKS;
+          const int64_t col = w.n0 + ch * PER;
+          const uint8_t* src = smem + r * ROW + ch * 16;
+          uint8_t* dst =
+              reinterpret_cast<uint8_t*>(p.d) + (d_off + (w.m0 + r0 + r) * N + col) * ESZ;
+          if (vec && col + PER <= N) {
+            *reinterpret_cast<int4*>(dst) = *reinterpret_cast<const int4*>(src);
+          } else {
+            for (int e = 0; e < PER && col + e < N; ++e) {
+              if constexpr (ESZ == 2)
+                reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+              else
+                reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src)[e];
+            }
           }
         }
       }
@@ -609,8 +639,9 @@ using CfgM32k2 = Cfg<128, 32, 4, 1, 3, 1, 2>;  // 32 x 32
 
 struct CfgInfo {
   int bm, bn, occ;
+  bool splitk;
 };
-#define FG8_CFG_INFO(C) {C::BM, C::BN, C::OCC}
+#define FG8_CFG_INFO(C) {C::BM, C::BN, C::OCC, C::SPLITK}
 static const CfgInfo kCfgs[] = {
     FG8_CFG_INFO(CfgBig),  FG8_CFG_INFO(CfgWide), FG8_CFG_INFO(CfgS32),  FG8_CFG_INFO(CfgS32x2),
     FG8_CFG_INFO(CfgS64),  FG8_CFG_INFO(CfgS128), FG8_CFG_INFO(CfgM64),  FG8_CFG_INFO(CfgM32),
@@ -642,7 +673,7 @@ static int dense_splits(int64_t tiles, int64_t kb, int slots) {
   if (tiles * 2 > slots || tiles > kSplitKMaxTiles) return 1;
   int64_t s = slots / tiles;
   if (s > kb / 2) s = kb / 2;
-  if (s > 16) s = 16;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   return (int)s;
 }
@@ -695,10 +726,11 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
     units = (int64_t)p.groups * ((p.M + t.bm - 1) / t.bm) * n_tiles;   // upper bound
   } else {
     const int64_t tiles = ((p.M + t.bm - 1) / t.bm) * n_tiles;
-    if (p.mode == kDense) {
+    if (p.mode == kDense && kCfgs[t.cfg].splitk) {
       t.splits = dense_splits(tiles, KB, slots);
       if (forced && forced_splits > 0 && tiles <= kSplitKMaxTiles)
         t.splits = (int)(forced_splits < KB ? forced_splits : KB);
+      if (t.splits > kMaxSplits) t.splits = kMaxSplits;
     }
     units = tiles * t.splits;
   }

@@ -36,6 +36,16 @@ __global__ void k_mfma32_scaled(const v8i* a, const v8i* b, const int* sa, const
   d[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], z, 0, 0, 0, sa[l], 0, sb[l]);
 }
 
+// D = A B + C with the accumulator input C loaded per lane.
+__global__ void k_mfma16_acc(const v8i* a, const v8i* b, const v4f* c, v4f* d) {
+  const int l = threadIdx.x;
+  d[l] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[l], b[l], c[l], 0, 0, 0, 0, 0, 0);
+}
+__global__ void k_mfma32_acc(const v8i* a, const v8i* b, const v16f* c, v16f* d) {
+  const int l = threadIdx.x;
+  d[l] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[l], b[l], c[l], 0, 0, 0, 0, 0, 0);
+}
+
 // n floats -> n/2 packed words (bytes 0 and 1 hold the two conversions).
 __global__ void k_cvt(const float* x, uint32_t* out, int npairs, int clamp) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -74,6 +84,16 @@ int probe_mfma32_scaled(const void* a, const void* b, const void* sa, const void
                         hipStream_t s) {
   hipLaunchKernelGGL(k_mfma32_scaled, dim3(1), dim3(64), 0, s, (const v8i*)a, (const v8i*)b,
                      (const int*)sa, (const int*)sb, (v16f*)d);
+  return (int)hipGetLastError();
+}
+int probe_mfma16_acc(const void* a, const void* b, const void* c, void* d, hipStream_t s) {
+  hipLaunchKernelGGL(k_mfma16_acc, dim3(1), dim3(64), 0, s, (const v8i*)a, (const v8i*)b,
+                     (const v4f*)c, (v4f*)d);
+  return (int)hipGetLastError();
+}
+int probe_mfma32_acc(const void* a, const void* b, const void* c, void* d, hipStream_t s) {
+  hipLaunchKernelGGL(k_mfma32_acc, dim3(1), dim3(64), 0, s, (const v8i*)a, (const v8i*)b,
+                     (const v16f*)c, (v16f*)d);
   return (int)hipGetLastError();
 }
 int probe_cvt_fp8(const void* x, void* out, int npairs, int clamp, hipStream_t s) {
