@@ -363,6 +363,36 @@ def run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launch
                    steps=20)
             del qa2, sa2, qw2, sw2, d2
 
+    # MoE contiguous W1 with MXFP8 operands from BF16 sources (the training
+    # pipeline: BF16 -> MXFP8 quantize -> grouped GEMM -> BF16)
+    if want("mxcontig"):
+        cc = inputs.ContiguousCase()
+        routing = inputs.zipf_topk_routing(cc.workload, cc.tokens, cc.experts, cc.topk)
+        lay = inputs.contiguous_layout(routing, cc.experts)
+        rt = torch.from_numpy(lay.row_token).to(dev)
+        live = rt >= 0
+        be = torch.from_numpy(lay.block_expert).to(dev)
+        x = randn((cc.tokens, cc.hidden), seed=21).bfloat16()
+        a1 = torch.zeros((lay.m_total, cc.hidden), dtype=torch.bfloat16, device=dev)
+        a1[live] = x[rt[live]]
+        del x
+        qa = torch.empty_like(a1, dtype=torch.uint8)
+        ea = torch.empty((lay.m_total, cc.hidden // 32), dtype=torch.uint8, device=dev)
+        record(f"quantize mx1x32 from bf16 {lay.m_total}x{cc.hidden}",
+               [lambda: fg8.fp8_quantize(a1, "mx", q=qa, scales=ea)],
+               nbytes=a1.numel() * 3 + a1.numel() // 32)
+        del a1
+        w1 = randn((cc.experts, cc.inter, cc.hidden), cc.hidden ** -0.5, seed=22).bfloat16()
+        qw, ew = fg8.fp8_quantize(w1, "mx")
+        del w1
+        d1 = torch.empty((lay.m_total, cc.inter), dtype=torch.bfloat16, device=dev)
+        fl = 2 * lay.valid_rows * cc.inter * cc.hidden
+        nb = qa.numel() + ea.numel() + qw.numel() + ew.numel() + 2 * d1.numel()
+        record(f"moe contiguous mxfp8 W1 {lay.m_total}(valid {lay.valid_rows})x{cc.inter}x{cc.hidden}",
+               [lambda: fg8.grouped_gemm_mxfp8_contiguous(qa, ea, qw, ew, be, out=d1)], fl, nb,
+               steps=20)
+        del qa, ea, qw, ew, d1
+
     # MoE masked, FP32 block scales and MXFP8
     if want("masked"):
         mc = inputs.MaskedCase()

@@ -97,6 +97,17 @@ fg8_status fp8_quantize(const float* x, int64_t batch, int64_t rows, int64_t col
                         fg8_scale_kind kind, uint8_t* q, void* scales, hipStream_t stream);
 
 /*
+ * fp8_quantize_bf16: fp8_quantize for a BF16 source, the BF16 -> MXFP8 step
+ * of the MoE training pipeline (aitrends.kr B200 article, MXFP8 section) and
+ * its 1x128 / 128x128 counterparts.  BF16 widens exactly to FP32, so the
+ * result is bit-identical to fp8_quantize of the widened tensor.
+ *   x  const uint16_t [batch][rows][cols] bfloat16 bit patterns, row-major;
+ *   every other argument, layout and error as fp8_quantize.
+ */
+fg8_status fp8_quantize_bf16(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                             fg8_scale_kind kind, uint8_t* q, void* scales, hipStream_t stream);
+
+/*
  * gemm_fp8_blockscaled: dense D = A B^T with 1x128 scales on A and 128x128
  * scales on B, two-level accumulation (DeepGEMM release news, ctol-kr.com,
  * section 1; shapes of the DeepGEMM explainer's speed-up table, opsoai.com).
@@ -172,6 +183,25 @@ fg8_status gemm_mxfp8(const uint8_t* a, const uint8_t* sa_e8m0, const uint8_t* b
                       const uint8_t* sb_e8m0, const int32_t* valid_rows, void* d, fg8_out out,
                       int32_t num_groups, int64_t m_per_group, int64_t n, int64_t k,
                       hipStream_t stream);
+
+/*
+ * grouped_gemm_mxfp8_contiguous: MoE grouped GEMM in the contiguous layout
+ * with MXFP8 operands (aitrends.kr B200 article, MXFP8 section: MXFP8 grouped
+ * GEMM for the experts of a DeepSeek-V3 MoE layer; the contiguous layout of
+ * the DeepGEMM release news, ctol-kr.com, section 4).  One E8M0 exponent per
+ * 32 consecutive K elements of every row of a and b, applied by the scaled
+ * MFMA.
+ *   a  uint8 [m_total][k]         sa_e8m0 uint8 [m_total][k/32]
+ *   b  uint8 [E][n][k]            sb_e8m0 uint8 [E][n][k/32]
+ *   block_expert, d, the skipping of out-of-range expert ids, sizes and errors
+ *   as grouped_gemm_fp8_contiguous; k % 128 == 0 (else FG8_EUNSUPPORTED).
+ *   E8M0 byte 0xFF (NaN) is not a valid input.
+ */
+fg8_status grouped_gemm_mxfp8_contiguous(const uint8_t* a, const uint8_t* sa_e8m0,
+                                         const uint8_t* b, const uint8_t* sb_e8m0,
+                                         const int32_t* block_expert, void* d, fg8_out out,
+                                         int64_t m_total, int64_t n, int64_t k,
+                                         int32_t num_experts, hipStream_t stream);
 
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* fg8_last_error(void);

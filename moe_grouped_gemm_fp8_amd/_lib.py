@@ -25,6 +25,7 @@ _c_ptr = ctypes.c_void_p
 
 _SIGNATURES = {
     "fp8_quantize": [_c_ptr, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr],
+    "fp8_quantize_bf16": [_c_ptr, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr],
     "gemm_fp8_blockscaled": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int, _c_i64, _c_i64,
                              _c_i64, _c_ptr, ctypes.c_size_t, _c_ptr],
     "grouped_gemm_fp8_contiguous": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int,
@@ -33,6 +34,8 @@ _SIGNATURES = {
                                 _c_i32, _c_i64, _c_i64, _c_i64, _c_ptr],
     "gemm_mxfp8": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int, _c_i32, _c_i64,
                    _c_i64, _c_i64, _c_ptr],
+    "grouped_gemm_mxfp8_contiguous": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int,
+                                      _c_i64, _c_i64, _c_i64, _c_i32, _c_ptr],
     "fg8_gemm_workspace_bytes": [_c_i64, _c_i64, _c_i64],
     "fg8_last_error": [],
     "fg8_version": [],
@@ -111,8 +114,10 @@ def version() -> int:
 
 # --------------------------------------------------------------- quantize
 def fp8_quantize(x, kind="1x128", q=None, scales=None):
-    """x float32 [..., rows, cols] -> (q uint8, scales); see fg8.h for layouts."""
-    _dev(x, torch.float32, "x")
+    """x float32 or bfloat16 [..., rows, cols] -> (q uint8, scales); see fg8.h
+    for layouts.  A bfloat16 source quantizes exactly like its float32 value."""
+    bf16 = x.dtype == torch.bfloat16
+    _dev(x, torch.bfloat16 if bf16 else torch.float32, "x")
     code = SCALE_KINDS[kind]
     *lead, rows, cols = x.shape
     batch = 1
@@ -128,7 +133,8 @@ def fp8_quantize(x, kind="1x128", q=None, scales=None):
                                  device=x.device)
         else:
             scales = torch.empty((*lead, rows, cols // 32), dtype=torch.uint8, device=x.device)
-    _check(lib().fp8_quantize(_ptr(x), batch, rows, cols, code, _ptr(q), _ptr(scales), _stream()))
+    fn = lib().fp8_quantize_bf16 if bf16 else lib().fp8_quantize
+    _check(fn(_ptr(x), batch, rows, cols, code, _ptr(q), _ptr(scales), _stream()))
     return q, scales
 
 
@@ -230,4 +236,25 @@ def gemm_mxfp8(a, sa, b, sb, valid_rows=None, out_dtype=torch.bfloat16, out=None
     _dev(out, out.dtype, "out")
     _check(lib().gemm_mxfp8(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(valid_rows), _ptr(out),
                             _out_code(out.dtype), G, m, n, k, _stream()))
+    return out
+
+
+def grouped_gemm_mxfp8_contiguous(a, sa, b, sb, block_expert, out_dtype=torch.bfloat16, out=None):
+    """Contiguous layout with MXFP8 operands: a [m_total, k], sa uint8
+    [m_total, k/32], b [E, n, k], sb uint8 [E, n, k/32], block_expert int32
+    [m_total/128]."""
+    _fp8(a, "a"); _fp8(b, "b")
+    _dev(sa, torch.uint8, "sa"); _dev(sb, torch.uint8, "sb")
+    _dev(block_expert, torch.int32, "block_expert")
+    m, k = a.shape
+    E, n, kb = b.shape
+    if kb != k or sa.shape != (m, k // 32) or sb.shape != (E, n, k // 32) \
+            or block_expert.shape != (m // 128,):
+        raise ValueError("operand shapes disagree")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _dev(out, out.dtype, "out")
+    _check(lib().grouped_gemm_mxfp8_contiguous(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
+                                               _ptr(block_expert), _ptr(out),
+                                               _out_code(out.dtype), m, n, k, E, _stream()))
     return out

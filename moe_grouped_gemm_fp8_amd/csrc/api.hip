@@ -61,13 +61,17 @@ fg8_status run(fg8::GemmProblem& p, const char* fn, hipStream_t stream) {
 
 extern "C" {
 
-int fg8_version(void) { return 100; }   // 0.1.0
+int fg8_version(void) { return 200; }   // 0.2.0
 
 const char* fg8_last_error(void) { return g_err; }
 
-fg8_status fp8_quantize(const float* x, int64_t batch, int64_t rows, int64_t cols,
-                        fg8_scale_kind kind, uint8_t* q, void* scales, hipStream_t stream) {
-  const char* fn = "fp8_quantize";
+}  // extern "C"
+
+namespace {
+
+fg8_status quantize_any(const char* fn, const void* x, bool bf16, int64_t batch, int64_t rows,
+                        int64_t cols, fg8_scale_kind kind, uint8_t* q, void* scales,
+                        hipStream_t stream) {
   FG8_CHECK_PTR(x);
   FG8_CHECK_PTR(q);
   FG8_CHECK_PTR(scales);
@@ -84,10 +88,25 @@ fg8_status fp8_quantize(const float* x, int64_t batch, int64_t rows, int64_t col
     return fail(FG8_EUNSUPPORTED, "%s: too many row blocks", fn);
   if (kind != FG8_SCALE_MX1x32 && cols / 128 >= 65536)
     return fail(FG8_EUNSUPPORTED, "%s: too many column blocks", fn);
-  const hipError_t e = fg8::launch_quantize(x, batch, rows, cols, (int)kind, q, scales, stream);
+  const hipError_t e =
+      fg8::launch_quantize(x, bf16, batch, rows, cols, (int)kind, q, scales, stream);
   if (e != hipSuccess) return fail(FG8_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   g_err[0] = 0;
   return FG8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fg8_status fp8_quantize(const float* x, int64_t batch, int64_t rows, int64_t cols,
+                        fg8_scale_kind kind, uint8_t* q, void* scales, hipStream_t stream) {
+  return quantize_any("fp8_quantize", x, false, batch, rows, cols, kind, q, scales, stream);
+}
+
+fg8_status fp8_quantize_bf16(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                             fg8_scale_kind kind, uint8_t* q, void* scales, hipStream_t stream) {
+  return quantize_any("fp8_quantize_bf16", x, true, batch, rows, cols, kind, q, scales, stream);
 }
 
 size_t fg8_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
@@ -208,6 +227,36 @@ fg8_status gemm_mxfp8(const uint8_t* a, const uint8_t* sa_e8m0, const uint8_t* b
   p.mx = 1;
   p.mode = fg8::kMasked; p.M = m_per_group; p.N = n; p.K = k; p.groups = num_groups;
   p.valid = valid_rows;
+  return run(p, fn, stream);
+}
+
+fg8_status grouped_gemm_mxfp8_contiguous(const uint8_t* a, const uint8_t* sa_e8m0,
+                                         const uint8_t* b, const uint8_t* sb_e8m0,
+                                         const int32_t* block_expert, void* d, fg8_out out,
+                                         int64_t m_total, int64_t n, int64_t k,
+                                         int32_t num_experts, hipStream_t stream) {
+  const char* fn = "grouped_gemm_mxfp8_contiguous";
+  FG8_CHECK_PTR(a);
+  FG8_CHECK_PTR(sa_e8m0);
+  FG8_CHECK_PTR(b);
+  FG8_CHECK_PTR(sb_e8m0);
+  FG8_CHECK_PTR(block_expert);
+  FG8_CHECK_PTR(d);
+  if (out != FG8_OUT_F32 && out != FG8_OUT_BF16) return fail(FG8_EINVAL, "%s: bad out", fn);
+  if (num_experts < 1) return fail(FG8_EINVAL, "%s: num_experts=%d", fn, (int)num_experts);
+  if (m_total < 1 || n < 1 || m_total >= kMaxDim || n >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: bad sizes m_total=%lld n=%lld", fn, (long long)m_total,
+                (long long)n);
+  if (m_total % 128)
+    return fail(FG8_EUNSUPPORTED, "%s: m_total=%lld is not a multiple of 128", fn,
+                (long long)m_total);
+  if (fg8_status s = check_k(fn, k)) return s;
+  fg8::GemmProblem p{};
+  p.a = a; p.sa = sa_e8m0; p.b = b; p.sb = sb_e8m0; p.d = d;
+  p.out_bf16 = out == FG8_OUT_BF16;
+  p.mx = 1;
+  p.mode = fg8::kContiguous; p.M = m_total; p.N = n; p.K = k; p.groups = num_experts;
+  p.block_expert = block_expert;
   return run(p, fn, stream);
 }
 

@@ -52,8 +52,8 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus);
 size_t splitk_workspace_bytes(int64_t m, int64_t n, int64_t k, int num_cus);
 hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t stream);
 
-hipError_t launch_quantize(const float* x, int64_t batch, int64_t rows, int64_t cols, int kind,
-                           uint8_t* q, void* scales, hipStream_t stream);
+hipError_t launch_quantize(const void* x, bool bf16, int64_t batch, int64_t rows, int64_t cols,
+                           int kind, uint8_t* q, void* scales, hipStream_t stream);
 
 int device_cu_count();
 

@@ -288,9 +288,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       }
     } else {
       ga = p.a;
-      gsa = (const float*)p.sa;
       gb = p.b + (int64_t)w.g * N * K;
-      gsb = (const float*)p.sb + (int64_t)w.g * nb_blocks * KB;
+      if constexpr (MX) {
+        gea = (const uint8_t*)p.sa;
+        geb = (const uint8_t*)p.sb + (int64_t)w.g * N * (K / kMxBlock);
+      } else {
+        gsa = (const float*)p.sa;
+        gsb = (const float*)p.sb + (int64_t)w.g * nb_blocks * KB;
+      }
     }
 
     // every wave must be done with the LDS stages of the previous unit
@@ -783,6 +788,7 @@ hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
         default: return launch<CfgBig, false, kDense>(p, t.grid, s);
       }
     case kContiguous:
+      if (p.mx) return launch<CfgWide8, true, kContiguous>(p, t.grid, s);
       if (t.cfg == kCfgWide8) return launch<CfgWide8, false, kContiguous>(p, t.grid, s);
       return launch<CfgWide, false, kContiguous>(p, t.grid, s);
     default:

@@ -1,4 +1,4 @@
-// FP32 -> e4m3 quantization with fine-grained scales.
+// FP32 or BF16 -> e4m3 quantization with fine-grained scales.
 //
 // Scale then convert: the FP32 tensor is multiplied by a scaling factor and
 // turned into FP8 (cuda-deepseek blog, hrletsgo.me, list item 5), per tile
@@ -19,6 +19,22 @@
 
 namespace fg8 {
 
+// Four consecutive source elements as float4.  BF16 sources (raw 16-bit
+// words) widen exactly, so a BF16 tensor quantizes exactly like its FP32
+// value.
+template <class T>
+__device__ __forceinline__ float4 load4(const T* p);
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+template <>
+__device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
 // ---------------------------------------------------------------- 1 x 128
 // Block: 256 threads = 4 waves; one block covers 32 rows x 128 columns (one
 // K group).  Each wave handles 8 rows, 2 rows per step: lanes 0-31 one row,
@@ -26,7 +42,8 @@ namespace fg8 {
 // so the 32 scales of a block are contiguous.
 constexpr int kQRowsPerBlock = 32;
 
-__global__ __launch_bounds__(256) void quant_1x128_kernel(const float* __restrict__ x,
+template <class T>
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const T* __restrict__ x,
                                                           uint8_t* __restrict__ q,
                                                           float* __restrict__ s, int64_t rows,
                                                           int64_t cols) {
@@ -34,7 +51,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const float* __restric
   const int kb = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t kblocks = cols / kGroup;
-  const float* xb = x + b * rows * cols;
+  const T* xb = x + b * rows * cols;
   uint8_t* qb = q + b * rows * cols;
   float* sb = s + b * kblocks * rows + (int64_t)kb * rows;
   const int64_t row0 = (int64_t)blockIdx.x * kQRowsPerBlock + wave * 8 + (lane >> 5);
@@ -44,8 +61,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const float* __restric
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int64_t r = row0 + 2 * st;
-    v[st] = r < rows ? *reinterpret_cast<const float4*>(xb + r * cols + col)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[st] = r < rows ? load4(xb + r * cols + col) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
@@ -64,7 +80,8 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const float* __restric
 // Block: 256 threads over one 128x128 block.  Thread t owns column chunk
 // (t % 32) * 4 of rows t / 32 + 8 i, i = 0..15: 16 float4 in registers, the
 // amax is reduced across the wave and then across the 4 waves through LDS.
-__global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restrict__ x,
+template <class T>
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const T* __restrict__ x,
                                                             uint8_t* __restrict__ q,
                                                             float* __restrict__ s, int64_t rows,
                                                             int64_t cols) {
@@ -74,7 +91,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
   const int tid = threadIdx.x;
   const int64_t kblocks = cols / kGroup;
   const int64_t rblocks = (rows + kGroup - 1) / kGroup;
-  const float* xb = x + b * rows * cols;
+  const T* xb = x + b * rows * cols;
   uint8_t* qb = q + b * rows * cols;
   const int64_t col = (int64_t)cb * kGroup + (tid & 31) * 4;
   const int64_t r0 = (int64_t)rb * kGroup + (tid >> 5);
@@ -84,8 +101,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t r = r0 + 8 * i;
-    v[i] = r < rows ? *reinterpret_cast<const float4*>(xb + r * cols + col)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[i] = r < rows ? load4(xb + r * cols + col) : make_float4(0.f, 0.f, 0.f, 0.f);
     m = fmaxf(m, abs_max4(v[i]));
   }
   m = group_max<64>(m);
@@ -108,13 +124,14 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const float* __restr
 // The tensor is a flat run of 32-element blocks (cols % 32 == 0, so no block
 // crosses a row) and the E8M0 array is indexed by the same block number.
 // Eight lanes hold one block; a grid-stride loop walks the blocks.
-__global__ __launch_bounds__(256) void quant_mx_kernel(const float* __restrict__ x,
+template <class T>
+__global__ __launch_bounds__(256) void quant_mx_kernel(const T* __restrict__ x,
                                                        uint8_t* __restrict__ q,
                                                        uint8_t* __restrict__ e, int64_t nblocks) {
   const int64_t stride = (int64_t)gridDim.x * 32;   // blocks per grid sweep (256 threads / 8)
   const int sub = threadIdx.x & 7;
   for (int64_t blk = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); blk < nblocks; blk += stride) {
-    const float4 v = *reinterpret_cast<const float4*>(x + blk * kMxBlock + sub * 4);
+    const float4 v = load4(x + blk * kMxBlock + sub * 4);
     const float amax = group_max<8>(abs_max4(v));
     // floor(log2 amax) - 8 from the exponent field; subnormal or zero amax
     // lands below -127 and is clamped there with the largest normal result.
@@ -127,25 +144,33 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const float* __restrict__
   }
 }
 
-hipError_t launch_quantize(const float* x, int64_t batch, int64_t rows, int64_t cols, int kind,
-                           uint8_t* q, void* scales, hipStream_t stream) {
+template <class T>
+static hipError_t launch_quantize_t(const T* x, int64_t batch, int64_t rows, int64_t cols, int kind,
+                                    uint8_t* q, void* scales, hipStream_t stream) {
   if (kind == 0) {
     dim3 grid((unsigned)((rows + kQRowsPerBlock - 1) / kQRowsPerBlock), (unsigned)(cols / kGroup),
               (unsigned)batch);
-    hipLaunchKernelGGL(quant_1x128_kernel, grid, dim3(256), 0, stream, x, q, (float*)scales, rows,
-                       cols);
+    hipLaunchKernelGGL(quant_1x128_kernel<T>, grid, dim3(256), 0, stream, x, q, (float*)scales,
+                       rows, cols);
   } else if (kind == 1) {
     dim3 grid((unsigned)(cols / kGroup), (unsigned)((rows + kGroup - 1) / kGroup), (unsigned)batch);
-    hipLaunchKernelGGL(quant_128x128_kernel, grid, dim3(256), 0, stream, x, q, (float*)scales,
+    hipLaunchKernelGGL(quant_128x128_kernel<T>, grid, dim3(256), 0, stream, x, q, (float*)scales,
                        rows, cols);
   } else {
     const int64_t nblocks = batch * rows * cols / kMxBlock;
     const int64_t want = (nblocks + 31) / 32;
     const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
-    hipLaunchKernelGGL(quant_mx_kernel, dim3(grid), dim3(256), 0, stream, x, q,
+    hipLaunchKernelGGL(quant_mx_kernel<T>, dim3(grid), dim3(256), 0, stream, x, q,
                        (uint8_t*)scales, nblocks);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, bool bf16, int64_t batch, int64_t rows, int64_t cols,
+                           int kind, uint8_t* q, void* scales, hipStream_t stream) {
+  if (bf16)
+    return launch_quantize_t((const uint16_t*)x, batch, rows, cols, kind, q, scales, stream);
+  return launch_quantize_t((const float*)x, batch, rows, cols, kind, q, scales, stream);
 }
 
 }  // namespace fg8

@@ -122,6 +122,28 @@ def gemm_mx(qa, ea, qb, eb, valid=None):
     return C, S
 
 
+def grouped_contiguous_mx(qa, ea, qb, eb, block_expert):
+    """Contiguous-layout grouped GEMM with MXFP8 operands (aitrends.kr B200
+    article, MXFP8 section: MXFP8 grouped GEMM for the MoE experts; layout as
+    grouped_contiguous).  qa [M_total, K], ea [M_total, K/32], qb [E, N, K],
+    eb [E, N, K/32]; block_expert[i] names the expert of rows [128 i, 128 i +
+    128).  Returns (C, S), each [M_total, N]; blocks whose expert id is
+    outside [0, E) are left NaN (undefined)."""
+    qa = np.asarray(qa)
+    M, K = qa.shape
+    E, N, _ = qb.shape
+    be = np.asarray(block_expert)
+    assert M % GROUP == 0 and be.shape == (M // GROUP,)
+    A = dequant_mx(qa, ea)
+    C = np.full((M, N), np.nan)
+    S = np.full((M, N), np.nan)
+    for e in range(E):
+        rows = np.repeat(be == e, GROUP)
+        if rows.any():
+            C[rows], S[rows] = matmul_with_base(A[rows], dequant_mx(qb[e], eb[e]))
+    return C, S
+
+
 def round_to_bf16(c) -> np.ndarray:
     """float64 -> nearest bfloat16 (8 significant bits), ties to even, as the
     float32 value that bfloat16 holds.  Finite inputs within bfloat16 range."""

@@ -30,14 +30,15 @@ def test_header_lists_the_five_entry_points():
     names = _declared()
     for n in ("fp8_quantize", "gemm_fp8_blockscaled", "grouped_gemm_fp8_contiguous",
               "grouped_gemm_fp8_masked", "gemm_mxfp8", "fg8_gemm_workspace_bytes",
-              "fg8_last_error", "fg8_version"):
+              "fg8_last_error", "fg8_version", "fp8_quantize_bf16",
+              "grouped_gemm_mxfp8_contiguous"):
         assert n in names
 
 
 def test_every_declared_symbol_is_exported(L):
     for n in _declared():
         assert hasattr(L, n), f"{n} declared in fg8.h but not exported"
-    assert L.fg8_version() == 100
+    assert L.fg8_version() == 200
 
 
 P = ctypes.c_void_p
@@ -98,3 +99,18 @@ def test_grouped_validation(L):
     assert x(ok, ok, ok, ok, None, ok, 0, 0, 64, 64, 256, None) == 1
     assert x(ok, ok, ok, ok, _fake(0x10008), ok, 0, 2, 64, 64, 256, None) == 1
     assert x(ok, ok, ok, ok, None, ok, 0, 2, 64, 64, 96, None) == 2
+
+
+def test_bf16_quantize_and_mx_contiguous_validation(L):
+    ok = _fake(0x10000)
+    q = L.fp8_quantize_bf16
+    assert q(None, 1, 1, 128, 0, ok, ok, None) == 1
+    assert b"x is NULL" in L.fg8_last_error()
+    assert q(_fake(0x10002), 1, 1, 128, 0, ok, ok, None) == 1
+    assert q(ok, 1, 1, 100, 2, ok, ok, None) == 2
+    c = L.grouped_gemm_mxfp8_contiguous
+    assert c(ok, ok, ok, ok, None, ok, 0, 256, 64, 256, 4, None) == 1
+    assert b"block_expert is NULL" in L.fg8_last_error()
+    assert c(ok, ok, ok, ok, ok, ok, 0, 200, 64, 256, 4, None) == 2
+    assert c(ok, ok, ok, ok, ok, ok, 0, 256, 64, 96, 4, None) == 2
+    assert c(ok, ok, ok, ok, ok, ok, 0, 256, 64, 256, 0, None) == 1

@@ -141,6 +141,78 @@ def test_contiguous_full_size_sampled(dev, which):
         check_bf16(out[np.ix_(rows, cols)], C, S, K, f"{which} expert {e}", S_flush=F)
 
 
+# ------------------------------------------------------------- MXFP8 contiguous
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(300, 512, 384, 6, 2), (700, 1024, 200, 9, 3)])
+def test_contiguous_mx_small(dev, shape, out_dtype):
+    c, (lay, a1, w1, a2, w2) = _small_contiguous(*shape)
+    qa, ea = scaling.quantize_mx(a1)
+    qb, eb = scaling.quantize_mx(w1)
+    C, S = gemm.grouped_contiguous_mx(qa, ea, qb, eb, lay.block_expert)
+    ta, tea, tb, teb, tbe = _gpu(qa, ea, qb, eb, lay.block_expert)
+    d = fg8.grouped_gemm_mxfp8_contiguous(ta, tea, tb, teb, tbe, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    F = np.zeros_like(C)
+    for e in range(c.experts):
+        rows = np.repeat(lay.block_expert == e, 128)
+        if rows.any():
+            F[rows] = ref_mx(qa[rows], ea[rows], qb[e], eb[e])[2]
+    _check(_bits(d), C, S, c.hidden, "mx contiguous small", derived=False, F=F)
+
+
+def test_contiguous_mx_out_of_range_ids_skip_their_block(dev):
+    c, (lay, a1, w1, a2, w2) = _small_contiguous(300, 512, 384, 6, 2)
+    qa, ea = scaling.quantize_mx(a1)
+    qb, eb = scaling.quantize_mx(w1)
+    C, S = gemm.grouped_contiguous_mx(qa, ea, qb, eb, lay.block_expert)
+    be = lay.block_expert.copy()
+    be[1] = -7
+    ta, tea, tb, teb, tbe = _gpu(qa, ea, qb, eb, be)
+    out = torch.full((qa.shape[0], qb.shape[1]), float(SENTINEL_F32), dtype=torch.float32,
+                     device="cuda")
+    fg8.grouped_gemm_mxfp8_contiguous(ta, tea, tb, teb, tbe, out=out)
+    torch.cuda.synchronize()
+    d = out.cpu().numpy()
+    bad = np.repeat(np.arange(be.size) == 1, 128)
+    assert np.all(d[bad] == SENTINEL_F32)
+    check_f32(d[~bad], C[~bad], S[~bad], c.hidden, "mx contiguous good blocks", derived=False)
+
+
+def test_contiguous_mx_bf16_sources_full_size_sampled(dev):
+    """The MXFP8 training pipeline at the MoE W1 size: BF16 activations and
+    weights quantized to MXFP8 on the GPU, then the contiguous grouped GEMM.
+    The oracle quantizes the same BF16 values (widened) itself and checks
+    sampled rows of every expert against two 128-column blocks."""
+    c = inputs.ContiguousCase()
+    lay, a1, w1, a2, w2 = inputs.contiguous_case(c)
+    del a2, w2
+    tA = torch.from_numpy(a1).cuda().bfloat16()
+    tW = torch.from_numpy(w1).cuda().bfloat16()
+    A = tA.float().cpu().numpy()               # the BF16 values, widened exactly
+    qa, ea = fg8.fp8_quantize(tA, "mx")
+    qb, eb = fg8.fp8_quantize(tW, "mx")
+    W = tW.float().cpu().numpy()
+    del tA, tW, a1, w1
+    tbe = torch.from_numpy(lay.block_expert).cuda()
+    d = fg8.grouped_gemm_mxfp8_contiguous(qa, ea, qb, eb, tbe, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    out = _bits(d)
+    g = np.random.default_rng(402)
+    N, K = W.shape[1], A.shape[1]
+    nbs = g.choice(N // 128, 2, replace=False)
+    cols = np.concatenate([np.arange(nb * 128, nb * 128 + 128) for nb in nbs])
+    for e in range(c.experts):
+        blocks = np.nonzero(lay.block_expert == e)[0]
+        if blocks.size == 0:
+            continue
+        own = np.concatenate([np.arange(b * 128, b * 128 + 128) for b in blocks])
+        rows = np.unique(np.concatenate([own[:8], own[-1:], g.choice(own, 8)]))
+        qa_o, ea_o = scaling.quantize_mx(A[rows])
+        qb_o, eb_o = scaling.quantize_mx(W[e][cols])
+        C, S, F = ref_mx(qa_o, ea_o, qb_o, eb_o)
+        check_bf16(out[np.ix_(rows, cols)], C, S, K, f"mx bf16 expert {e}", S_flush=F)
+
+
 # ------------------------------------------------------------- masked
 def _masked_inputs(E, cap, N, K, workload=41, valid=None):
     mc = inputs.MaskedCase(experts=E, cap=cap, N=N, K=K, workload=workload)

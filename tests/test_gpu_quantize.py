@@ -101,3 +101,30 @@ def test_repeatable(dev):
     a = _run(x, "1x128")
     b = _run(x, "1x128")
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _to_bf16(x):
+    """float32 -> nearest bfloat16 (ties to even) and the float32 it holds;
+    the test's inputs only, so plain bit arithmetic is enough (finite x)."""
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return r, (r.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["1x128", "128x128", "mx"])
+@pytest.mark.parametrize("shape", [(5, 256), (2, 130, 384), (64, 7168)])
+def test_bf16_source_bit_exact(dev, kind, shape):
+    """A BF16 tensor quantizes exactly like its (exactly widened) FP32 value:
+    codes and scales equal the oracle's on the widened tensor."""
+    bits, wide = _to_bf16(_hard_values(np.random.default_rng(203), shape))
+    t = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    q, s = fg8.fp8_quantize(t, kind)
+    torch.cuda.synchronize()
+    q, s = q.cpu().numpy(), s.cpu().numpy()
+    ref = {"1x128": scaling.quantize_1x128, "128x128": scaling.quantize_128x128,
+           "mx": scaling.quantize_mx}[kind](wide)
+    assert np.array_equal(q, ref[0])
+    if kind == "mx":
+        assert np.array_equal(s, ref[1])
+    else:
+        assert np.array_equal(s.view(np.uint32), ref[1].view(np.uint32))

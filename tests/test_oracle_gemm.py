@@ -194,3 +194,39 @@ def test_quantize_then_gemm_tracks_fp32_product():
     C, S = gemm.gemm_blockscaled(qa, sa, qb, sb)
     ref = A.astype(np.float64) @ B.astype(np.float64).T
     assert np.all(np.abs(C - ref) <= 0.13 * S + 1e-12)
+
+
+def test_contiguous_mx_reduces_to_mx_per_block():
+    """Each 128-row block of the MXFP8 contiguous product is the MX product of
+    those rows with its expert's B; blocks with an out-of-range id stay
+    undefined (NaN)."""
+    g = np.random.default_rng(17)
+    E, N, K = 3, 96, 256
+    be = np.array([2, 0, 0, 5, 1], np.int32)          # id 5 is out of range
+    M = be.size * 128
+    qa, qb = _rand_codes(g, (M, K)), _rand_codes(g, (E, N, K))
+    ea = g.integers(110, 140, (M, K // 32)).astype(np.uint8)
+    eb = g.integers(110, 140, (E, N, K // 32)).astype(np.uint8)
+    C, S = gemm.grouped_contiguous_mx(qa, ea, qb, eb, be)
+    for i, e in enumerate(be):
+        r = slice(i * 128, (i + 1) * 128)
+        if e >= E:
+            assert np.all(np.isnan(C[r])) and np.all(np.isnan(S[r]))
+            continue
+        Cd, Sd = gemm.gemm_mx(qa[None, r], ea[None, r], qb[None, e], eb[None, e])
+        assert np.array_equal(C[r], Cd[0]) and np.array_equal(S[r], Sd[0])
+
+
+def test_contiguous_mx_equals_blockscaled_with_unit_scales():
+    """With every E8M0 byte 127 (scale 1) the MX contiguous product equals the
+    block-scaled contiguous product with unit FP32 scales."""
+    g = np.random.default_rng(18)
+    E, N, K = 2, 130, 256
+    be = np.array([1, 0, 1], np.int32)
+    M = be.size * 128
+    qa, qb = _rand_codes(g, (M, K)), _rand_codes(g, (E, N, K))
+    C, S = gemm.grouped_contiguous_mx(qa, np.full((M, K // 32), 127, np.uint8), qb,
+                                      np.full((E, N, K // 32), 127, np.uint8), be)
+    Cb, Sb = gemm.grouped_contiguous(qa, np.ones((K // 128, M), np.float32), qb,
+                                     np.ones((E, 2, K // 128), np.float32), be)
+    assert np.array_equal(C, Cb) and np.array_equal(S, Sb)
