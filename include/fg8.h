@@ -203,6 +203,45 @@ fg8_status grouped_gemm_mxfp8_contiguous(const uint8_t* a, const uint8_t* sa_e8m
                                          int64_t m_total, int64_t n, int64_t k,
                                          int32_t num_experts, hipStream_t stream);
 
+/*
+ * moe_contiguous_layout_fp8: the step before grouped_gemm_fp8_contiguous.
+ * From the router's top-k expert ids it builds the contiguous layout of the
+ * DeepGEMM release news (ctol-kr.com, section 4 "MoE": the tokens of every
+ * expert stacked one expert after another, each expert's run padded to the
+ * 128-row M block, one expert index per block) and writes the 1x128
+ * quantization of the gathered token rows, all on the device (the counts
+ * never visit the host).
+ *   x          [tokens][hidden] float (x_is_bf16 = 0) or bfloat16 bits (1)
+ *   topk_ids   int32 [tokens][topk]: expert ids; a repeated id in a row
+ *              counts once, ids outside [0, num_experts) route nowhere
+ *   q          uint8 [m_cap][hidden]       sa float [hidden/128][m_cap]
+ *              (the a / sa operands of grouped_gemm_fp8_contiguous)
+ *   block_expert   int32 [m_cap/128]: expert of each 128-row block, -1 for
+ *              the blocks past the last run (the contiguous GEMM skips them)
+ *   row_token  int32 [m_cap]: source token of each row, -1 for padding
+ *   expert_offsets int32 [num_experts + 1]: first row of each expert's run;
+ *              expert_offsets[num_experts] = rows in use
+ *   expert_counts  int32 [num_experts]: tokens routed to each expert
+ * Experts are laid out in id order, an expert's tokens in ascending token
+ * order.  Padding rows quantize as zeros (code 0, scale 1), so every output
+ * is written and the result is the same on every call.
+ *   hidden % 128 == 0 (else FG8_EUNSUPPORTED); tokens >= 1;
+ *   1 <= topk <= 256; 1 <= num_experts <= 1024; m_cap % 128 == 0 and
+ *   m_cap >= fg8_moe_capacity(tokens, topk, num_experts), which holds any
+ *   routing (else FG8_EINVAL).
+ */
+fg8_status moe_contiguous_layout_fp8(const void* x, int32_t x_is_bf16, int64_t tokens,
+                                     int64_t hidden, const int32_t* topk_ids, int32_t topk,
+                                     int32_t num_experts, int64_t m_cap, uint8_t* q, float* sa,
+                                     int32_t* block_expert, int32_t* row_token,
+                                     int32_t* expert_offsets, int32_t* expert_counts,
+                                     hipStream_t stream);
+
+/* Rows that hold any routing of `tokens` tokens with `topk` ids each over
+ * `num_experts` experts: every routed row plus up to 127 padding rows per
+ * expert, rounded up to whole 128-row blocks (0 for arguments out of range). */
+int64_t fg8_moe_capacity(int64_t tokens, int32_t topk, int32_t num_experts);
+
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* fg8_last_error(void);
 

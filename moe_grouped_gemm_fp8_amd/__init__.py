@@ -13,5 +13,7 @@ from ._lib import (  # noqa: F401
     grouped_gemm_fp8_contiguous,
     grouped_gemm_fp8_masked,
     grouped_gemm_mxfp8_contiguous,
+    moe_capacity,
+    moe_contiguous_layout_fp8,
     version,
 )

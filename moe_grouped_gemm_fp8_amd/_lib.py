@@ -36,11 +36,15 @@ _SIGNATURES = {
                    _c_i64, _c_i64, _c_ptr],
     "grouped_gemm_mxfp8_contiguous": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int,
                                       _c_i64, _c_i64, _c_i64, _c_i32, _c_ptr],
+    "moe_contiguous_layout_fp8": [_c_ptr, _c_i32, _c_i64, _c_i64, _c_ptr, _c_i32, _c_i32, _c_i64,
+                                  _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr],
+    "fg8_moe_capacity": [_c_i64, _c_i32, _c_i32],
     "fg8_gemm_workspace_bytes": [_c_i64, _c_i64, _c_i64],
     "fg8_last_error": [],
     "fg8_version": [],
 }
-_RESTYPES = {"fg8_gemm_workspace_bytes": ctypes.c_size_t, "fg8_last_error": ctypes.c_char_p}
+_RESTYPES = {"fg8_gemm_workspace_bytes": ctypes.c_size_t, "fg8_last_error": ctypes.c_char_p,
+             "fg8_moe_capacity": ctypes.c_int64}
 
 _lib = None
 _lock = threading.Lock()
@@ -257,4 +261,46 @@ def grouped_gemm_mxfp8_contiguous(a, sa, b, sb, block_expert, out_dtype=torch.bf
     _check(lib().grouped_gemm_mxfp8_contiguous(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
                                                _ptr(block_expert), _ptr(out),
                                                _out_code(out.dtype), m, n, k, E, _stream()))
+    return out
+
+
+# --------------------------------------------------------------- MoE routing
+def moe_capacity(tokens, topk, num_experts) -> int:
+    """Rows of a contiguous layout that hold any routing of these sizes."""
+    return int(lib().fg8_moe_capacity(tokens, topk, num_experts))
+
+
+def moe_contiguous_layout_fp8(x, topk_ids, num_experts, m_cap=None, out=None):
+    """x float32 or bfloat16 [tokens, hidden], topk_ids int32 [tokens, topk]
+    (device) -> dict of q uint8 [m_cap, hidden], sa [hidden/128, m_cap],
+    block_expert int32 [m_cap/128], row_token int32 [m_cap],
+    expert_offsets int32 [E + 1], expert_counts int32 [E], all on the device:
+    the operands of grouped_gemm_fp8_contiguous plus the row map.  `out`, a
+    dict like the one returned, gives the buffers to fill."""
+    bf16 = x.dtype == torch.bfloat16
+    _dev(x, torch.bfloat16 if bf16 else torch.float32, "x")
+    _dev(topk_ids, torch.int32, "topk_ids")
+    tokens, hidden = x.shape
+    if topk_ids.dim() != 2 or topk_ids.shape[0] != tokens:
+        raise ValueError("topk_ids must be [tokens, topk]")
+    topk = topk_ids.shape[1]
+    if m_cap is None:
+        m_cap = moe_capacity(tokens, topk, num_experts)
+    dev = x.device
+    shapes = {"q": ((m_cap, hidden), torch.uint8), "sa": ((hidden // 128, m_cap), torch.float32),
+              "block_expert": ((m_cap // 128,), torch.int32), "row_token": ((m_cap,), torch.int32),
+              "expert_offsets": ((num_experts + 1,), torch.int32),
+              "expert_counts": ((num_experts,), torch.int32)}
+    if out is not None:
+        for name, (shape, dtype) in shapes.items():
+            _dev(out[name], dtype, name)
+            if tuple(out[name].shape) != shape:
+                raise ValueError(f"{name} must have shape {shape}")
+    else:
+        out = {name: torch.empty(shape, dtype=dtype, device=dev)
+               for name, (shape, dtype) in shapes.items()}
+    _check(lib().moe_contiguous_layout_fp8(
+        _ptr(x), int(bf16), tokens, hidden, _ptr(topk_ids), topk, num_experts, m_cap,
+        _ptr(out["q"]), _ptr(out["sa"]), _ptr(out["block_expert"]), _ptr(out["row_token"]),
+        _ptr(out["expert_offsets"]), _ptr(out["expert_counts"]), _stream()))
     return out

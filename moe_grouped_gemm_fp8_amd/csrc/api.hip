@@ -61,7 +61,7 @@ fg8_status run(fg8::GemmProblem& p, const char* fn, hipStream_t stream) {
 
 extern "C" {
 
-int fg8_version(void) { return 200; }   // 0.2.0
+int fg8_version(void) { return 300; }   // 0.3.0
 
 const char* fg8_last_error(void) { return g_err; }
 
@@ -258,6 +258,51 @@ fg8_status grouped_gemm_mxfp8_contiguous(const uint8_t* a, const uint8_t* sa_e8m
   p.mode = fg8::kContiguous; p.M = m_total; p.N = n; p.K = k; p.groups = num_experts;
   p.block_expert = block_expert;
   return run(p, fn, stream);
+}
+
+int64_t fg8_moe_capacity(int64_t tokens, int32_t topk, int32_t num_experts) {
+  if (tokens < 1 || tokens >= kMaxDim || topk < 1 || topk > 256 || num_experts < 1 ||
+      num_experts > 1024)
+    return 0;
+  return (tokens * topk + (int64_t)num_experts * 127 + 127) / 128 * 128;
+}
+
+fg8_status moe_contiguous_layout_fp8(const void* x, int32_t x_is_bf16, int64_t tokens,
+                                     int64_t hidden, const int32_t* topk_ids, int32_t topk,
+                                     int32_t num_experts, int64_t m_cap, uint8_t* q, float* sa,
+                                     int32_t* block_expert, int32_t* row_token,
+                                     int32_t* expert_offsets, int32_t* expert_counts,
+                                     hipStream_t stream) {
+  const char* fn = "moe_contiguous_layout_fp8";
+  FG8_CHECK_PTR(x);
+  FG8_CHECK_PTR(topk_ids);
+  FG8_CHECK_PTR(q);
+  FG8_CHECK_PTR(sa);
+  FG8_CHECK_PTR(block_expert);
+  FG8_CHECK_PTR(row_token);
+  FG8_CHECK_PTR(expert_offsets);
+  FG8_CHECK_PTR(expert_counts);
+  if (x_is_bf16 != 0 && x_is_bf16 != 1)
+    return fail(FG8_EINVAL, "%s: x_is_bf16=%d must be 0 or 1", fn, (int)x_is_bf16);
+  if (tokens < 1 || tokens >= kMaxDim || hidden < 1 || hidden >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: bad sizes tokens=%lld hidden=%lld", fn, (long long)tokens,
+                (long long)hidden);
+  if (topk < 1 || topk > 256) return fail(FG8_EINVAL, "%s: topk=%d must be in [1, 256]", fn, topk);
+  if (num_experts < 1 || num_experts > 1024)
+    return fail(FG8_EINVAL, "%s: num_experts=%d must be in [1, 1024]", fn, (int)num_experts);
+  if (hidden % 128 || hidden / 128 >= 65536)
+    return fail(FG8_EUNSUPPORTED, "%s: hidden=%lld must be a multiple of 128 below 2^23", fn,
+                (long long)hidden);
+  const int64_t need = fg8_moe_capacity(tokens, topk, num_experts);
+  if (m_cap % 128 || m_cap < need || m_cap >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: m_cap=%lld must be a multiple of 128 in [%lld, 2^31)", fn,
+                (long long)m_cap, (long long)need);
+  const hipError_t e = fg8::launch_route_quantize(x, x_is_bf16 == 1, tokens, hidden, topk_ids, topk,
+                                                  num_experts, m_cap, q, sa, block_expert,
+                                                  row_token, expert_counts, expert_offsets, stream);
+  if (e != hipSuccess) return fail(FG8_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  g_err[0] = 0;
+  return FG8_OK;
 }
 
 }  // extern "C"

@@ -39,11 +39,13 @@ __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* p) {
 // Block: 256 threads = 4 waves; one block covers 32 rows x 128 columns (one
 // K group).  Each wave handles 8 rows, 2 rows per step: lanes 0-31 one row,
 // lanes 32-63 the next, 4 floats per lane.  Scales are written K-block major,
-// so the 32 scales of a block are contiguous.
+// so the 32 scales of a block are contiguous.  With GATHER, output row r
+// quantizes source row row_src[r] (a row of zeros where that is negative).
 constexpr int kQRowsPerBlock = 32;
 
-template <class T>
+template <class T, bool GATHER>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const T* __restrict__ x,
+                                                          const int32_t* __restrict__ row_src,
                                                           uint8_t* __restrict__ q,
                                                           float* __restrict__ s, int64_t rows,
                                                           int64_t cols) {
@@ -61,7 +63,9 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const T* __restrict__ 
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int64_t r = row0 + 2 * st;
-    v[st] = r < rows ? load4(xb + r * cols + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    int64_t src = r < rows ? r : -1;
+    if constexpr (GATHER) src = r < rows ? row_src[r] : -1;
+    v[st] = src >= 0 ? load4(xb + src * cols + col) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
@@ -150,8 +154,8 @@ static hipError_t launch_quantize_t(const T* x, int64_t batch, int64_t rows, int
   if (kind == 0) {
     dim3 grid((unsigned)((rows + kQRowsPerBlock - 1) / kQRowsPerBlock), (unsigned)(cols / kGroup),
               (unsigned)batch);
-    hipLaunchKernelGGL(quant_1x128_kernel<T>, grid, dim3(256), 0, stream, x, q, (float*)scales,
-                       rows, cols);
+    hipLaunchKernelGGL((quant_1x128_kernel<T, false>), grid, dim3(256), 0, stream, x, nullptr, q,
+                       (float*)scales, rows, cols);
   } else if (kind == 1) {
     dim3 grid((unsigned)(cols / kGroup), (unsigned)((rows + kGroup - 1) / kGroup), (unsigned)batch);
     hipLaunchKernelGGL(quant_128x128_kernel<T>, grid, dim3(256), 0, stream, x, q, (float*)scales,
@@ -171,6 +175,18 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t batch, int64_t rows
   if (bf16)
     return launch_quantize_t((const uint16_t*)x, batch, rows, cols, kind, q, scales, stream);
   return launch_quantize_t((const float*)x, batch, rows, cols, kind, q, scales, stream);
+}
+
+hipError_t launch_quantize_gather(const void* x, bool bf16, const int32_t* row_src, int64_t rows,
+                                  int64_t cols, uint8_t* q, float* scales, hipStream_t stream) {
+  const dim3 grid((unsigned)((rows + kQRowsPerBlock - 1) / kQRowsPerBlock), (unsigned)(cols / kGroup));
+  if (bf16)
+    hipLaunchKernelGGL((quant_1x128_kernel<uint16_t, true>), grid, dim3(256), 0, stream,
+                       (const uint16_t*)x, row_src, q, scales, rows, cols);
+  else
+    hipLaunchKernelGGL((quant_1x128_kernel<float, true>), grid, dim3(256), 0, stream,
+                       (const float*)x, row_src, q, scales, rows, cols);
+  return hipGetLastError();
 }
 
 }  // namespace fg8

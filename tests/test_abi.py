@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "fg8.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:fg8_status|size_t|const char\*|int)\s+(\w+)\s*\(", text, re.M)
+    names = re.findall(r"^\s*(?:fg8_status|size_t|const char\*|int64_t|int)\s+(\w+)\s*\(", text, re.M)
     return sorted(set(names))
 
 
@@ -31,14 +31,15 @@ def test_header_lists_the_five_entry_points():
     for n in ("fp8_quantize", "gemm_fp8_blockscaled", "grouped_gemm_fp8_contiguous",
               "grouped_gemm_fp8_masked", "gemm_mxfp8", "fg8_gemm_workspace_bytes",
               "fg8_last_error", "fg8_version", "fp8_quantize_bf16",
-              "grouped_gemm_mxfp8_contiguous"):
+              "grouped_gemm_mxfp8_contiguous", "moe_contiguous_layout_fp8",
+              "fg8_moe_capacity"):
         assert n in names
 
 
 def test_every_declared_symbol_is_exported(L):
     for n in _declared():
         assert hasattr(L, n), f"{n} declared in fg8.h but not exported"
-    assert L.fg8_version() == 200
+    assert L.fg8_version() == 300
 
 
 P = ctypes.c_void_p
@@ -114,3 +115,35 @@ def test_bf16_quantize_and_mx_contiguous_validation(L):
     assert c(ok, ok, ok, ok, ok, ok, 0, 200, 64, 256, 4, None) == 2
     assert c(ok, ok, ok, ok, ok, ok, 0, 256, 64, 96, 4, None) == 2
     assert c(ok, ok, ok, ok, ok, ok, 0, 256, 64, 256, 0, None) == 1
+
+
+def test_moe_capacity_host_logic(L):
+    cap = L.fg8_moe_capacity
+    cap.restype = ctypes.c_int64
+    assert cap(8192, 8, 32) == 69632            # 65536 routed rows + 32 * 127, in 128-row blocks
+    assert cap(1, 1, 1) == 128
+    assert cap(5, 2, 3) == 512                   # (10 + 381) rounded up to 512
+    assert cap(0, 8, 32) == 0 and cap(8, 0, 32) == 0 and cap(8, 8, 0) == 0
+    assert cap(8, 8, 1025) == 0 and cap(8, 257, 4) == 0
+
+
+def test_moe_layout_validation(L):
+    ok = _fake(0x10000)
+    f = L.moe_contiguous_layout_fp8
+    f.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, P, ctypes.c_int32,
+                  ctypes.c_int32, ctypes.c_int64, P, P, P, P, P, P, P]
+
+    def call(x=ok, bf16=0, tokens=8192, hidden=7168, ids=ok, topk=8, experts=32, m_cap=69632,
+             offsets=ok):
+        return f(x, bf16, tokens, hidden, ids, topk, experts, m_cap, ok, ok, ok, ok, offsets, ok,
+                 None)
+
+    assert call(ids=None) == 1 and b"topk_ids is NULL" in L.fg8_last_error()
+    assert call(offsets=_fake(0x10004)) == 1 and b"16-byte" in L.fg8_last_error()
+    assert call(bf16=2) == 1
+    assert call(tokens=0) == 1
+    assert call(topk=0) == 1 and call(topk=257) == 1
+    assert call(experts=0) == 1 and call(experts=1025) == 1
+    assert call(hidden=7100) == 2
+    assert call(m_cap=69632 - 128) == 1 and b"m_cap" in L.fg8_last_error()
+    assert call(m_cap=69632 + 64) == 1
