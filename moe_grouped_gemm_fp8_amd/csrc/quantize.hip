@@ -36,48 +36,118 @@ __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* p) {
 }
 
 // ---------------------------------------------------------------- 1 x 128
-// Block: 256 threads = 4 waves; one block covers 32 rows x 128 columns (one
-// K group).  Each wave handles 8 rows, 2 rows per step: lanes 0-31 one row,
-// lanes 32-63 the next, 4 floats per lane.  Scales are written K-block major,
-// so the 32 scales of a block are contiguous.  With GATHER, output row r
-// quantizes source row row_src[r] (a row of zeros where that is negative).
-constexpr int kQRowsPerBlock = 32;
+// Row streaming: a wave owns one run of columns of one row (the whole row when
+// there are enough rows to fill the chip, else a shorter run) and walks it with
+// 16-byte loads, kQUnroll of them in flight per lane.  One load instruction of
+// a wave covers 64 x 16 bytes = 2 (FP32) or 4 (BF16) groups of 128 columns; the
+// 32 or 16 lanes that hold a group reduce its amax with butterfly exchanges.
+// Scales are written K-block major.  With GATHER, output row r quantizes source
+// row row_src[r] (a row of zeros where that is negative).
+constexpr int kQUnroll = 8;
+
+template <class T>
+struct RowVec;
+template <>
+struct RowVec<float> {
+  static constexpr int kElems = 4;
+  __device__ static void widen(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+  }
+};
+template <>
+struct RowVec<uint16_t> {   // BF16 bits widen exactly to FP32
+  static constexpr int kElems = 8;
+  __device__ static void widen(const uint4& u, float* f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
 
 template <class T, bool GATHER>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const T* __restrict__ x,
                                                           const int32_t* __restrict__ row_src,
                                                           uint8_t* __restrict__ q,
                                                           float* __restrict__ s, int64_t rows,
-                                                          int64_t cols) {
-  const int64_t b = blockIdx.z;
-  const int kb = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t kblocks = cols / kGroup;
-  const T* xb = x + b * rows * cols;
-  uint8_t* qb = q + b * rows * cols;
-  float* sb = s + b * kblocks * rows + (int64_t)kb * rows;
-  const int64_t row0 = (int64_t)blockIdx.x * kQRowsPerBlock + wave * 8 + (lane >> 5);
-  const int64_t col = (int64_t)kb * kGroup + (lane & 31) * 4;
-
-  float4 v[4];
+                                                          int64_t cols, int64_t seg_cols,
+                                                          int64_t items) {
+  constexpr int EPL = RowVec<T>::kElems;   // elements per lane per load
+  constexpr int LPG = kGroup / EPL;        // lanes per 128-column group
+  constexpr int SPAN = 64 * EPL;           // columns per wave load
+  const int lane = threadIdx.x & 63;
+  const int64_t nseg = (cols + seg_cols - 1) / seg_cols;
+  // waves walk the items independently (there is no barrier in this kernel)
+  for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < items;
+       it += (int64_t)gridDim.x * 4) {
+    const int64_t grow = it / nseg;               // row over all batches
+    const int64_t c_begin = (it - grow * nseg) * seg_cols;
+    const int64_t c_end = c_begin + seg_cols < cols ? c_begin + seg_cols : cols;
+    const int64_t b = grow / rows, r = grow - b * rows;
+    int64_t src = grow;
+    if constexpr (GATHER) src = row_src[grow];
+    const T* xr = x + (src >= 0 ? src : 0) * cols;
+    uint8_t* qr = q + grow * cols;
+    float* sb = s + b * (cols / kGroup) * rows + r;
+    for (int64_t c0 = c_begin; c0 < c_end; c0 += kQUnroll * SPAN) {
+      uint4 raw[kQUnroll];
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const int64_t r = row0 + 2 * st;
-    int64_t src = r < rows ? r : -1;
-    if constexpr (GATHER) src = r < rows ? row_src[r] : -1;
-    v[st] = src >= 0 ? load4(xb + src * cols + col) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+      for (int u = 0; u < kQUnroll; ++u) {
+        const int64_t col = c0 + u * SPAN + lane * EPL;
+        raw[u] = src >= 0 && col < c_end ? *reinterpret_cast<const uint4*>(xr + col)
+                                         : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const int64_t r = row0 + 2 * st;
-    const float amax = group_max<32>(abs_max4(v[st]));
-    const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
-    if (r < rows) {
-      const float4 y = make_float4(v[st].x / sc, v[st].y / sc, v[st].z / sc, v[st].w / sc);
-      *reinterpret_cast<uint32_t*>(qb + r * cols + col) = pack4_e4m3(y);
-      if ((lane & 31) == 0) sb[r] = sc;
+      for (int u = 0; u < kQUnroll; ++u) {
+        const int64_t col = c0 + u * SPAN + lane * EPL;
+        float f[EPL];
+        RowVec<T>::widen(raw[u], f);
+        float m = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) m = fmaxf(m, fabsf(f[e]));
+        const float amax = group_max<LPG>(m);
+        const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
+        if (col < c_end) {
+          uint32_t code[EPL / 4];
+#pragma unroll
+          for (int e = 0; e < EPL / 4; ++e)
+            code[e] = pack4_e4m3(make_float4(f[4 * e] / sc, f[4 * e + 1] / sc, f[4 * e + 2] / sc,
+                                             f[4 * e + 3] / sc));
+          if constexpr (EPL == 4)
+            *reinterpret_cast<uint32_t*>(qr + col) = code[0];
+          else
+            *reinterpret_cast<uint2*>(qr + col) = make_uint2(code[0], code[1]);
+          if ((lane & (LPG - 1)) == 0) sb[(col / kGroup) * rows] = sc;
+        }
+      }
     }
   }
+}
+
+// Column-run length for the 1x128 kernel: whole rows when the rows alone give
+// enough waves to fill the chip, else runs of whole wave loads.
+static int64_t q1_seg_cols(int64_t rows, int64_t cols, int elems) {
+  const int64_t span = 64 * (int64_t)elems;
+  const int64_t spans = (cols + span - 1) / span;
+  constexpr int64_t kTargetWaves = 8192;
+  int64_t per = rows * spans / kTargetWaves;
+  per = per < 1 ? 1 : per > spans ? spans : per;
+  return per * span;
+}
+
+template <class T, bool GATHER>
+static hipError_t launch_q1(const T* x, const int32_t* row_src, int64_t rows_all, int64_t rows,
+                            int64_t cols, uint8_t* q, float* s, hipStream_t stream) {
+  const int64_t seg = q1_seg_cols(rows_all, cols, RowVec<T>::kElems);
+  const int64_t items = rows_all * ((cols + seg - 1) / seg);
+  const int64_t blocks = (items + 3) / 4;
+  const unsigned grid = (unsigned)(blocks < (1 << 20) ? blocks : (1 << 20));
+  hipLaunchKernelGGL((quant_1x128_kernel<T, GATHER>), dim3(grid), dim3(256), 0, stream, x, row_src,
+                     q, s, rows, cols, seg, items);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- 128 x 128
@@ -152,10 +222,7 @@ template <class T>
 static hipError_t launch_quantize_t(const T* x, int64_t batch, int64_t rows, int64_t cols, int kind,
                                     uint8_t* q, void* scales, hipStream_t stream) {
   if (kind == 0) {
-    dim3 grid((unsigned)((rows + kQRowsPerBlock - 1) / kQRowsPerBlock), (unsigned)(cols / kGroup),
-              (unsigned)batch);
-    hipLaunchKernelGGL((quant_1x128_kernel<T, false>), grid, dim3(256), 0, stream, x, nullptr, q,
-                       (float*)scales, rows, cols);
+    return launch_q1<T, false>(x, nullptr, batch * rows, rows, cols, q, (float*)scales, stream);
   } else if (kind == 1) {
     dim3 grid((unsigned)(cols / kGroup), (unsigned)((rows + kGroup - 1) / kGroup), (unsigned)batch);
     hipLaunchKernelGGL(quant_128x128_kernel<T>, grid, dim3(256), 0, stream, x, q, (float*)scales,
@@ -179,14 +246,10 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t batch, int64_t rows
 
 hipError_t launch_quantize_gather(const void* x, bool bf16, const int32_t* row_src, int64_t rows,
                                   int64_t cols, uint8_t* q, float* scales, hipStream_t stream) {
-  const dim3 grid((unsigned)((rows + kQRowsPerBlock - 1) / kQRowsPerBlock), (unsigned)(cols / kGroup));
   if (bf16)
-    hipLaunchKernelGGL((quant_1x128_kernel<uint16_t, true>), grid, dim3(256), 0, stream,
-                       (const uint16_t*)x, row_src, q, scales, rows, cols);
-  else
-    hipLaunchKernelGGL((quant_1x128_kernel<float, true>), grid, dim3(256), 0, stream,
-                       (const float*)x, row_src, q, scales, rows, cols);
-  return hipGetLastError();
+    return launch_q1<uint16_t, true>((const uint16_t*)x, row_src, rows, rows, cols, q, scales,
+                                     stream);
+  return launch_q1<float, true>((const float*)x, row_src, rows, rows, cols, q, scales, stream);
 }
 
 }  // namespace fg8
