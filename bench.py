@@ -347,7 +347,19 @@ def run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launch
             record(f"moe contiguous W1 {lay.m_total}(valid {lay.valid_rows})x{cc.inter}x{cc.hidden}",
                    [lambda: fg8.grouped_gemm_fp8_contiguous(qa1, sa1, qw1, sw1, be, out=d1)], fl, nb,
                    steps=20)
-            del qa1, sa1, qw1, sw1, d1
+            # the same W1 GEMM with the SiLU-gated activation and the 1x128
+            # quantization of W2's input fused into the epilogue (the weight
+            # rows read as interleaved gate / up blocks)
+            qh = torch.empty((lay.m_total, cc.inter // 2), dtype=torch.uint8, device=dev)
+            sh = torch.empty((cc.inter // 256, lay.m_total), dtype=torch.float32, device=dev)
+            nb = (lay.m_total * cc.hidden + qw1.numel() + 4 * sa1.numel() + 4 * sw1.numel()
+                  + qh.numel() + 4 * sh.numel())
+            record(f"moe contiguous W1 + SiLU-gated activation + 1x128 quantize "
+                   f"{lay.m_total}(valid {lay.valid_rows})x{cc.inter}x{cc.hidden}",
+                   [lambda: fg8.grouped_gemm_fp8_contiguous_swiglu(qa1, sa1, qw1, sw1, be,
+                                                                    q_out=qh, s_out=sh)],
+                   fl, nb, steps=20)
+            del qa1, sa1, qw1, sw1, d1, qh, sh
             a2 = randn((lay.m_total, cc.inter2), seed=23)
             a2[~live] = 0
             qa2, sa2 = fg8.fp8_quantize(a2, "1x128")

@@ -204,6 +204,34 @@ fg8_status grouped_gemm_mxfp8_contiguous(const uint8_t* a, const uint8_t* sa_e8m
                                          int32_t num_experts, hipStream_t stream);
 
 /*
+ * grouped_gemm_fp8_contiguous_swiglu: the contiguous grouped GEMM of the
+ * first expert weight W1 with its activation and the quantization of the
+ * second GEMM's input fused into the epilogue, so the W1 product never
+ * reaches memory.  The pages give the expert layer as quantize -> grouped
+ * GEMM -> restore (aitrends.kr B200 article, MXFP8 pipeline diagram) with a
+ * W1 twice as wide as W2's input; the activation between the two GEMMs is
+ * not named there, and this library reads it as a SiLU-gated unit:
+ *   h[m][128 j + c] = silu(G[m][256 j + c]) * G[m][256 j + 128 + c],
+ *   silu(x) = x / (1 + e^-x),   G = the contiguous product A W1^T in FP32,
+ * i.e. the rows of W1 (and of its 128x128 scales) interleave in 128-row
+ * blocks: gate block j at rows 256 j .. 256 j + 127, up block j at rows
+ * 256 j + 128 .. 256 j + 255.  h is quantized 1x128 exactly as fp8_quantize
+ * does it (from the FP32 h the kernel computes):
+ *   a, sa, b [E][n][k], sb [E][n/128][k/128], block_expert: as
+ *            grouped_gemm_fp8_contiguous (b interleaved as above)
+ *   q_out    uint8 [m_total][n/2]       s_out  float [n/256][m_total]
+ *            (the a / sa operands of the contiguous GEMM with W2, k = n/2)
+ * Blocks whose block_expert is out of range are skipped (their rows of q_out
+ * and s_out are left as they were); padding rows of a (zeros) give q = 0,
+ * s = 1.  n % 256 == 0 and k % 128 == 0 (else FG8_EUNSUPPORTED).
+ */
+fg8_status grouped_gemm_fp8_contiguous_swiglu(const uint8_t* a, const float* sa,
+                                              const uint8_t* b, const float* sb,
+                                              const int32_t* block_expert, uint8_t* q_out,
+                                              float* s_out, int64_t m_total, int64_t n, int64_t k,
+                                              int32_t num_experts, hipStream_t stream);
+
+/*
  * moe_contiguous_layout_fp8: the step before grouped_gemm_fp8_contiguous.
  * From the router's top-k expert ids it builds the contiguous layout of the
  * DeepGEMM release news (ctol-kr.com, section 4 "MoE": the tokens of every

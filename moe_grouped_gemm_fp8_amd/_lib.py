@@ -30,6 +30,8 @@ _SIGNATURES = {
                              _c_i64, _c_ptr, ctypes.c_size_t, _c_ptr],
     "grouped_gemm_fp8_contiguous": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int,
                                     _c_i64, _c_i64, _c_i64, _c_i32, _c_ptr],
+    "grouped_gemm_fp8_contiguous_swiglu": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                           _c_i64, _c_i64, _c_i64, _c_i32, _c_ptr],
     "grouped_gemm_fp8_masked": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int,
                                 _c_i32, _c_i64, _c_i64, _c_i64, _c_ptr],
     "gemm_mxfp8": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int, _c_i32, _c_i64,
@@ -201,6 +203,34 @@ def grouped_gemm_fp8_contiguous(a, sa, b, sb, block_expert, out_dtype=torch.bflo
                                              _ptr(block_expert), _ptr(out), _out_code(out.dtype),
                                              m, n, k, E, _stream()))
     return out
+
+
+def grouped_gemm_fp8_contiguous_swiglu(a, sa, b, sb, block_expert, q_out=None, s_out=None):
+    """The contiguous grouped GEMM with W1 (rows interleaved in 128-row gate /
+    up blocks, see fg8.h) and the SiLU-gated activation plus its 1x128
+    quantization fused into the epilogue: a [m_total, k], sa [k/128, m_total],
+    b [E, n, k], sb [E, n/128, k/128], block_expert int32 [m_total/128] ->
+    (q_out uint8 [m_total, n/2], s_out float32 [n/256, m_total]).  Rows of
+    skipped blocks (expert id out of range) are left as they were."""
+    _fp8(a, "a"); _fp8(b, "b")
+    _dev(sa, torch.float32, "sa"); _dev(sb, torch.float32, "sb")
+    _dev(block_expert, torch.int32, "block_expert")
+    m, k = a.shape
+    E, n, kb = b.shape
+    if kb != k or sa.shape != (k // 128, m) or sb.shape != (E, -(-n // 128), k // 128) \
+            or block_expert.shape != (m // 128,):
+        raise ValueError("operand shapes disagree")
+    if q_out is None:
+        q_out = torch.empty((m, n // 2), dtype=torch.uint8, device=a.device)
+    if s_out is None:
+        s_out = torch.empty((n // 256, m), dtype=torch.float32, device=a.device)
+    _dev(q_out, torch.uint8, "q_out"); _dev(s_out, torch.float32, "s_out")
+    if q_out.shape != (m, n // 2) or s_out.shape != (n // 256, m):
+        raise ValueError("output shapes disagree")
+    _check(lib().grouped_gemm_fp8_contiguous_swiglu(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb),
+                                                    _ptr(block_expert), _ptr(q_out), _ptr(s_out),
+                                                    m, n, k, E, _stream()))
+    return q_out, s_out
 
 
 def grouped_gemm_fp8_masked(a, sa, b, sb, valid_rows, out_dtype=torch.bfloat16, out=None):

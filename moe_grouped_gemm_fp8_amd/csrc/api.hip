@@ -61,7 +61,7 @@ fg8_status run(fg8::GemmProblem& p, const char* fn, hipStream_t stream) {
 
 extern "C" {
 
-int fg8_version(void) { return 300; }   // 0.3.0
+int fg8_version(void) { return 400; }   // 0.4.0
 
 const char* fg8_last_error(void) { return g_err; }
 
@@ -174,6 +174,38 @@ fg8_status grouped_gemm_fp8_contiguous(const uint8_t* a, const float* sa, const 
   p.out_bf16 = out == FG8_OUT_BF16;
   p.mode = fg8::kContiguous; p.M = m_total; p.N = n; p.K = k; p.groups = num_experts;
   p.block_expert = block_expert;
+  return run(p, fn, stream);
+}
+
+fg8_status grouped_gemm_fp8_contiguous_swiglu(const uint8_t* a, const float* sa,
+                                              const uint8_t* b, const float* sb,
+                                              const int32_t* block_expert, uint8_t* q_out,
+                                              float* s_out, int64_t m_total, int64_t n, int64_t k,
+                                              int32_t num_experts, hipStream_t stream) {
+  const char* fn = "grouped_gemm_fp8_contiguous_swiglu";
+  FG8_CHECK_PTR(a);
+  FG8_CHECK_PTR(sa);
+  FG8_CHECK_PTR(b);
+  FG8_CHECK_PTR(sb);
+  FG8_CHECK_PTR(block_expert);
+  FG8_CHECK_PTR(q_out);
+  FG8_CHECK_PTR(s_out);
+  if (num_experts < 1) return fail(FG8_EINVAL, "%s: num_experts=%d", fn, (int)num_experts);
+  if (m_total < 1 || n < 1 || m_total >= kMaxDim || n >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: bad sizes m_total=%lld n=%lld", fn, (long long)m_total,
+                (long long)n);
+  if (m_total % 128)
+    return fail(FG8_EUNSUPPORTED, "%s: m_total=%lld is not a multiple of 128", fn,
+                (long long)m_total);
+  if (n % 256)
+    return fail(FG8_EUNSUPPORTED, "%s: n=%lld is not a multiple of 256 (gate/up block pairs)", fn,
+                (long long)n);
+  if (fg8_status s = check_k(fn, k)) return s;
+  fg8::GemmProblem p{};
+  p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.d = nullptr;
+  p.mode = fg8::kContiguous; p.M = m_total; p.N = n; p.K = k; p.groups = num_experts;
+  p.block_expert = block_expert;
+  p.swiglu = 1; p.q_out = q_out; p.s_out = s_out;
   return run(p, fn, stream);
 }
 

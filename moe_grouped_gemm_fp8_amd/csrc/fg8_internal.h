@@ -25,6 +25,12 @@ struct GemmProblem {
   const int32_t* block_expert;  // contiguous: expert of each 128-row block
   const int32_t* valid;         // masked: live rows per group (NULL = all M)
   int rotate;                   // 1: start each unit's K walk at a unit-dependent block
+  // contiguous only: 1 = fused SiLU-gated epilogue that writes the 1x128
+  // quantization of h = silu(gate) * up (W1 rows interleaved in 128-row
+  // gate/up blocks) to q_out [M][N/2] and s_out [N/256][M] instead of d
+  int swiglu;
+  uint8_t* q_out;
+  float* s_out;
   // split-K (dense only)
   int splits;
   float* ws_partial;

@@ -163,6 +163,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 __device__ __forceinline__ void wait_all_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// x * sigmoid(x) in FP32; -0 for very negative x (e^-x overflows to inf).
+__device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
+
 struct Unit {
   int g;            // group (expert)
   int64_t m0, n0;   // tile origin inside the group
@@ -564,10 +567,52 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
         __hip_atomic_store(p.ws_counters + w.tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
+    __syncthreads();   // every wave is done with the stage buffers
+
+    // ---- fused gated epilogue (contiguous layout, FP32 scales): the tile's
+    // first 128 columns are a gate block and the last 128 the matching up
+    // block, so its 128 outputs h = silu(gate) * up of each row form exactly
+    // one 1x128 group of the next GEMM's input; they are quantized here
+    // (amax, s = amax / 448, codes of h / s) and written as FP8 codes plus a
+    // K-block-major scale, instead of the BF16 / FP32 product.
+    if constexpr (MODE == kContiguous && !MX) {
+      if (p.swiglu) {
+        constexpr int ROW = C::BN * 4 + 16;
+        static_assert(C::BN == 2 * kGroup, "one gate block and one up block per tile");
+        static_assert(C::BM * ROW <= C::STAGES * C::STAGE_BYTES, "the FP32 tile fits in LDS");
+#pragma unroll
+        for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              *reinterpret_cast<float*>(smem + (wm0 + tm * 16 + 4 * (lane >> 4) + v) * ROW +
+                                        (wn0 + tn * 16 + (lane & 15)) * 4) = acc[tm][tn][v];
+        __syncthreads();
+        const int64_t NH = N / 2;
+        const int64_t hb = w.n0 / C::BN;   // 128-column block of h
+        uint8_t* qo = p.q_out + w.m0 * NH + hb * kGroup;
+        float* so = p.s_out + hb * M + w.m0;
+        const int c = (lane & 31) * 4;
+        // two rows per wave step (lanes 0-31 and 32-63), four columns a lane
+        for (int r = wave * 2 + (lane >> 5); r < C::BM; r += 2 * C::WAVES) {
+          const float4 g = *reinterpret_cast<const float4*>(smem + r * ROW + c * 4);
+          const float4 v = *reinterpret_cast<const float4*>(smem + r * ROW + (kGroup + c) * 4);
+          const float4 h = make_float4(silu(g.x) * v.x, silu(g.y) * v.y, silu(g.z) * v.z,
+                                       silu(g.w) * v.w);
+          const float amax = group_max<32>(abs_max4(h));
+          const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
+          *reinterpret_cast<uint32_t*>(qo + r * NH + c) =
+              pack4_e4m3(make_float4(h.x / sc, h.y / sc, h.z / sc, h.w / sc));
+          if ((lane & 31) == 0) so[r] = sc;
+        }
+        continue;   // the next unit starts with a barrier before reusing LDS
+      }
+    }
+
     // ---- epilogue: the tile is staged in LDS in the output type so that the
     // global stores are 16-byte pieces of rows; FP32 or BF16 (RNE); rows past
     // the live count and columns past N are not written.
-    __syncthreads();   // every wave is done with the stage buffers
     auto store_tile = [&](auto esz_c) {
       constexpr int ESZ = decltype(esz_c)::value;
       constexpr int ROW = C::BN * ESZ + 16;   // padded LDS row: conflict-free writes

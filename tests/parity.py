@@ -28,10 +28,20 @@ Inside one FP8 MFMA the 128 products are summed in groups of 16 consecutive
 BF16 outputs: within 1 BF16 ulp of the oracle rounded to BF16 (ordered-bit
   distance, +0 == -0), or, where FP32 accumulation alone moves a value near
   cancellation by more than that, |g - C| <= ulp_bf16(RNE(C)) + eps_acc * S.
+Fused gated epilogue (FP8 codes and 1x128 scales of h = silu(gate) * up):
+  the GPU's gate and up values lie within the GEMM bar T of the oracle's;
+  silu has slope below 1.1, so its h lies within
+  Eh = 1.1 Tg (|up| + Tu) + |silu(gate)| Tu, plus 2^-20 relative for the
+  FP32 evaluation.  Quantization is monotone, so the GPU's scale must lie
+  between the scales of the smallest and largest amax that h can have, and
+  each code, taken with the GPU's own scale, between the codes of
+  (h - Eh) / s and (h + Eh) / s.  Codes and scales are integer-valued
+  decisions made from FP32 values the oracle cannot reproduce bit for bit;
+  these bounds are what any correct implementation satisfies.
 """
 import numpy as np
 
-from oracle import e4m3, gemm
+from oracle import activation, e4m3, gemm
 from oracle.gemm import round_to_bf16
 
 
@@ -137,3 +147,41 @@ def ref_mx(qa, ea, qb, eb):
     eb64 = np.asarray(eb, np.float64) - 127.0
     scale = lambda m, n, g: np.exp2(ea64[m, g // 2] + eb64[n, g // 2])
     return C, S, trunc_bound(qa, qb, scale)
+
+
+def check_swiglu_quant(q, s, C, S, F, K, where=""):
+    """q uint8 [R, H] and s float32 [H/128, R]: the GPU's codes and scales of
+    h for R rows and H columns of h; C, S, F [R, 2H]: the oracle's product
+    with the interleaved W1 (same column blocks, same order), its base and
+    S_trunc (NaN where not computed: the stated bar is used there)."""
+    C, S = np.asarray(C, np.float64), np.asarray(S, np.float64)
+    F = np.broadcast_to(np.asarray(F, np.float64), C.shape)
+    T = np.where(np.isfinite(F), eps_acc(K) * S + np.nan_to_num(F), 1e-3 * S + 1e-6)
+    g, u = activation.gate_up_of(C)
+    Tg, Tu = activation.gate_up_of(T)
+    h = activation.swiglu_interleaved(C)
+    E0 = 1.1 * Tg * (np.abs(u) + Tu) + np.abs(activation.silu(g)) * Tu
+    Eh = E0 + 2.0 ** -20 * (np.abs(h) + E0)
+    R, H = h.shape
+    s_gpu = np.asarray(s, np.float32).astype(np.float64).T          # [R, H/128]
+    assert s_gpu.shape == (R, H // 128)
+    ha = np.abs(h).reshape(R, H // 128, 128)
+    Eg = Eh.reshape(R, H // 128, 128)
+    amax_lo = np.maximum(ha - Eg, 0.0).max(axis=2)
+    amax_hi = (ha + Eg).max(axis=2)
+    s_lo = np.float32(amax_lo / 448.0).astype(np.float64) * (1 - 2.0 ** -30)
+    s_hi = np.float32(amax_hi / 448.0).astype(np.float64) * (1 + 2.0 ** -30)
+    ok_s = ((s_gpu >= s_lo) & (s_gpu <= s_hi) & (amax_lo > 0)) | ((amax_lo == 0) & (
+        (s_gpu == 1.0) | ((s_gpu <= s_hi) & (amax_hi > 0))))
+    assert ok_s.all(), f"{where}: {np.count_nonzero(~ok_s)} scales outside their bounds"
+    sf = np.repeat(s_gpu, 128, axis=1)
+    lo_v = (h - Eh) / sf
+    hi_v = (h + Eh) / sf
+    lo_v = lo_v - np.abs(lo_v) * 2.0 ** -30
+    hi_v = hi_v + np.abs(hi_v) * 2.0 ** -30
+    lo = e4m3.round_to_e4m3_value(np.clip(lo_v, -1e4, 1e4))
+    hi = e4m3.round_to_e4m3_value(np.clip(hi_v, -1e4, 1e4))
+    dq = e4m3.decode(np.asarray(q, np.uint8))
+    ok = (dq >= lo) & (dq <= hi)
+    assert ok.all(), f"{where}: {np.count_nonzero(~ok)} of {ok.size} codes outside their bounds"
+    return int(np.count_nonzero(dq != e4m3.round_to_e4m3_value(np.float32(h / sf))))

@@ -32,14 +32,14 @@ def test_header_lists_the_five_entry_points():
               "grouped_gemm_fp8_masked", "gemm_mxfp8", "fg8_gemm_workspace_bytes",
               "fg8_last_error", "fg8_version", "fp8_quantize_bf16",
               "grouped_gemm_mxfp8_contiguous", "moe_contiguous_layout_fp8",
-              "fg8_moe_capacity"):
+              "fg8_moe_capacity", "grouped_gemm_fp8_contiguous_swiglu"):
         assert n in names
 
 
 def test_every_declared_symbol_is_exported(L):
     for n in _declared():
         assert hasattr(L, n), f"{n} declared in fg8.h but not exported"
-    assert L.fg8_version() == 300
+    assert L.fg8_version() == 400
 
 
 P = ctypes.c_void_p
@@ -147,3 +147,16 @@ def test_moe_layout_validation(L):
     assert call(hidden=7100) == 2
     assert call(m_cap=69632 - 128) == 1 and b"m_cap" in L.fg8_last_error()
     assert call(m_cap=69632 + 64) == 1
+
+
+def test_swiglu_validation(L):
+    ok = _fake(0x10000)
+    f = L.grouped_gemm_fp8_contiguous_swiglu
+    f.argtypes = [P] * 7 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, P]
+    assert f(ok, ok, ok, ok, ok, None, ok, 256, 512, 512, 4, None) == 1
+    assert b"q_out is NULL" in L.fg8_last_error()
+    assert f(ok, ok, ok, ok, ok, ok, ok, 256, 384, 512, 4, None) == 2      # n not a multiple of 256
+    assert b"gate/up" in L.fg8_last_error()
+    assert f(ok, ok, ok, ok, ok, ok, ok, 200, 512, 512, 4, None) == 2      # m_total % 128
+    assert f(ok, ok, ok, ok, ok, ok, ok, 256, 512, 500, 4, None) == 2      # k % 128
+    assert f(ok, ok, ok, ok, ok, ok, ok, 256, 512, 512, 0, None) == 1

@@ -1,5 +1,6 @@
 """CPU checks of the tolerance helpers in parity.py (no GPU)."""
 import numpy as np
+import pytest
 
 from oracle import e4m3
 from parity import check_f32, trunc_bound
@@ -53,3 +54,26 @@ def test_check_f32_skips_derived_bar_where_not_sampled():
         pass
     else:
         raise AssertionError("derived bar not applied")
+
+
+def test_swiglu_bounds_accept_the_oracle_and_reject_planted_mistakes():
+    """The fused-epilogue check passes the oracle's own quantization of h and
+    fails a swapped gate/up pairing and a scale off by 1%."""
+    from oracle import activation, scaling
+    from parity import check_swiglu_quant
+    g = np.random.default_rng(11)
+    C = g.standard_normal((16, 512)) * 2
+    S = np.abs(C) * 40 + 1.0
+    F = np.zeros_like(C)
+    h = np.float32(activation.swiglu_interleaved(C))
+    q, s = scaling.quantize_1x128(h)
+    check_swiglu_quant(q, s, C, S, F, 4096, "oracle")
+    gate, up = activation.gate_up_of(C)
+    swapped = np.concatenate([np.concatenate([up[:, 128 * j:128 * j + 128],
+                                              gate[:, 128 * j:128 * j + 128]], axis=1)
+                              for j in range(2)], axis=1)
+    qx, sx = scaling.quantize_1x128(np.float32(activation.swiglu_interleaved(swapped)))
+    with pytest.raises(AssertionError):
+        check_swiglu_quant(qx, sx, C, S, F, 4096, "swapped")
+    with pytest.raises(AssertionError):
+        check_swiglu_quant(q, s * np.float32(1.01), C, S, F, 4096, "scale")
