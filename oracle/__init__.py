@@ -10,4 +10,4 @@ pages and the mathematics fix (closed forms, hand-derived values under
 tests/golden/, exact rational brute force, exact special cases).  No function
 is left "parity unpinned".
 """
-from . import activation, e4m3, gemm, routing, scaling  # noqa: F401
+from . import activation, backward, e4m3, gemm, routing, scaling  # noqa: F401
