@@ -428,6 +428,41 @@ def run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launch
             / 1e9, 1)
         del x, ids, lay
 
+    # Training backward of W1: dY and X quantized along the token axis
+    # (transposed codes), then the K-grouped weight-gradient GEMM over the
+    # routing layout's expert row ranges, FP32 dW [32][4096][7168]
+    if want("wgrad"):
+        cc = inputs.ContiguousCase()
+        ids = torch.from_numpy(inputs.zipf_topk_routing(cc.workload, cc.tokens, cc.experts,
+                                                        cc.topk)).to(dev)
+        xb = randn((cc.tokens, cc.hidden), seed=21).bfloat16()
+        lay = fg8.moe_contiguous_layout_fp8(xb, ids, cc.experts)
+        offs = lay["expert_offsets"]
+        M = int(offs[-1].item())
+        rt = lay["row_token"][:M].long()
+        live = rt >= 0
+        X = torch.zeros((M, cc.hidden), dtype=torch.bfloat16, device=dev)
+        X[live] = xb[rt[live]]
+        dy = randn((M, cc.inter), seed=25).bfloat16()
+        dy[~live] = 0
+        del xb, lay
+        qx = torch.empty((cc.hidden, M), dtype=torch.uint8, device=dev)
+        sx = torch.empty((M // 128, cc.hidden), dtype=torch.float32, device=dev)
+        record(f"quantize 1x128 along tokens (transposed) from bf16 {M}x{cc.hidden}",
+               [lambda: fg8.fp8_quantize(X, "1x128_t", q=qx, scales=sx)],
+               nbytes=X.numel() * 3 + 4 * X.numel() // 128)
+        qy, sy = fg8.fp8_quantize(dy, "1x128_t")
+        del X, dy
+        dw = torch.empty((cc.experts, cc.inter, cc.hidden), dtype=torch.float32, device=dev)
+        valid = int(live.sum().item())
+        fl = 2 * valid * cc.inter * cc.hidden
+        nb = qy.numel() + qx.numel() + 4 * (sy.numel() + sx.numel()) + 4 * dw.numel()
+        record(f"moe wgrad W1 k-grouped {cc.experts}x{cc.inter}x{cc.hidden} over {M} rows "
+               f"(valid {valid}), FP32 out",
+               [lambda: fg8.grouped_gemm_fp8_kgrouped(qy, sy, qx, sx, offs, out=dw)], fl, nb,
+               steps=20)
+        del qx, sx, qy, sy, dw
+
     # MoE masked, FP32 block scales and MXFP8
     if want("masked"):
         mc = inputs.MaskedCase()

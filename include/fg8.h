@@ -76,7 +76,8 @@ typedef enum { FG8_OUT_F32 = 0, FG8_OUT_BF16 = 1 } fg8_out;
 typedef enum {
   FG8_SCALE_1x128 = 0,
   FG8_SCALE_128x128 = 1,
-  FG8_SCALE_MX1x32 = 2
+  FG8_SCALE_MX1x32 = 2,
+  FG8_SCALE_1x128_T = 3
 } fg8_scale_kind;
 
 /*
@@ -85,12 +86,18 @@ typedef enum {
  * mixed-precision loop, list item 5, at per-group granularity; MX variant per
  * the aitrends.kr MXFP8 glossary entry).
  *   x       const float [batch][rows][cols], row-major.
- *   q       uint8 [batch][rows][cols] e4m3 codes (output).
+ *   q       uint8 [batch][rows][cols] e4m3 codes (output); for
+ *           FG8_SCALE_1x128_T the transpose, [batch][cols][rows].
  *   scales  output, layout by kind:
  *             FG8_SCALE_1x128   float   [batch][cols/128][rows]  (K-block major)
  *             FG8_SCALE_128x128 float   [batch][ceil(rows/128)][cols/128]
  *             FG8_SCALE_MX1x32  uint8_t [batch][rows][cols/32]   (E8M0 bytes)
- *   batch >= 1, rows >= 1; cols % 128 == 0 (cols % 32 == 0 for MX), else
+ *             FG8_SCALE_1x128_T float   [batch][rows/128][cols]
+ *   FG8_SCALE_1x128_T groups 128 consecutive ROWS of each column: the 1x128
+ *   quantization of x^T, written as x^T (the token-axis layout the weight
+ *   gradient multiplies, see grouped_gemm_fp8_kgrouped).
+ *   batch >= 1, rows >= 1; cols % 128 == 0 (cols % 32 == 0 for MX; for
+ *   FG8_SCALE_1x128_T rows % 128 == 0 and cols % 64 == 0), else
  *   FG8_EUNSUPPORTED.  Results are bit-exact with the formats above.
  */
 fg8_status fp8_quantize(const float* x, int64_t batch, int64_t rows, int64_t cols,
@@ -230,6 +237,33 @@ fg8_status grouped_gemm_fp8_contiguous_swiglu(const uint8_t* a, const float* sa,
                                               const int32_t* block_expert, uint8_t* q_out,
                                               float* s_out, int64_t m_total, int64_t n, int64_t k,
                                               int32_t num_experts, hipStream_t stream);
+
+/*
+ * grouped_gemm_fp8_kgrouped: the weight-gradient GEMM of a grouped (MoE)
+ * linear layer, dW_e = dY_e^T X_e summed over the tokens routed to expert e.
+ * The pages say only that training computes its gradients in the same FP8 /
+ * FP32 mixed precision (cuda-deepseek blog, hrletsgo.me, backward-pass step
+ * of the training loop; aitrends.kr B200 article: FP8 grouped GEMMs for the
+ * DeepSeek-V3 experts in training); this layout is the library's reading.
+ * The token axis is K and is shared: group g multiplies the K range
+ * k_offsets[g] .. k_offsets[g+1] - 1 of both operands, both quantized 1x128
+ * along K (fp8_quantize with FG8_SCALE_1x128_T of dY and X gives them):
+ *   D[g][i][j] = sum_{k in group g} A[i][k] * B[j][k],
+ *   A[i][k] = e4m3(a[i][k]) * sa[k/128][i],  B[j][k] = e4m3(b[j][k]) * sb[k/128][j]
+ *   a  uint8 [m][k_total]      sa float [k_total/128][m]
+ *   b  uint8 [n][k_total]      sb float [k_total/128][n]
+ *   k_offsets  int32 [num_groups + 1], device memory: multiples of 128,
+ *              non-decreasing, in [0, k_total] (the contiguous layout's
+ *              expert_offsets); range-checked by the kernel (clamped)
+ *   d  [num_groups][m][n] float or bfloat16 bits; an empty group's block is
+ *      written with zeros.
+ *   k_total % 128 == 0 and 128 <= k_total <= 2^24 - 128 (else
+ *   FG8_EUNSUPPORTED); 1 <= num_groups <= 65536; m, n >= 1.
+ */
+fg8_status grouped_gemm_fp8_kgrouped(const uint8_t* a, const float* sa, const uint8_t* b,
+                                     const float* sb, const int32_t* k_offsets, void* d,
+                                     fg8_out out, int32_t num_groups, int64_t m, int64_t n,
+                                     int64_t k_total, hipStream_t stream);
 
 /*
  * moe_contiguous_layout_fp8: the step before grouped_gemm_fp8_contiguous.

@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     gemm_workspace_bytes,
     grouped_gemm_fp8_contiguous,
     grouped_gemm_fp8_contiguous_swiglu,
+    grouped_gemm_fp8_kgrouped,
     grouped_gemm_fp8_masked,
     grouped_gemm_mxfp8_contiguous,
     moe_capacity,

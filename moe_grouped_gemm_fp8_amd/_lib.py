@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libfg8.so")
 
 FG8_OK, FG8_EINVAL, FG8_EUNSUPPORTED, FG8_EHIP = 0, 1, 2, 3
 OUT_F32, OUT_BF16 = 0, 1
-SCALE_KINDS = {"1x128": 0, "128x128": 1, "mx": 2}
+SCALE_KINDS = {"1x128": 0, "128x128": 1, "mx": 2, "1x128_t": 3}
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -32,6 +32,8 @@ _SIGNATURES = {
                                     _c_i64, _c_i64, _c_i64, _c_i32, _c_ptr],
     "grouped_gemm_fp8_contiguous_swiglu": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                            _c_i64, _c_i64, _c_i64, _c_i32, _c_ptr],
+    "grouped_gemm_fp8_kgrouped": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int,
+                                  _c_i32, _c_i64, _c_i64, _c_i64, _c_ptr],
     "grouped_gemm_fp8_masked": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int,
                                 _c_i32, _c_i64, _c_i64, _c_i64, _c_ptr],
     "gemm_mxfp8": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int, _c_i32, _c_i64,
@@ -121,7 +123,8 @@ def version() -> int:
 # --------------------------------------------------------------- quantize
 def fp8_quantize(x, kind="1x128", q=None, scales=None):
     """x float32 or bfloat16 [..., rows, cols] -> (q uint8, scales); see fg8.h
-    for layouts.  A bfloat16 source quantizes exactly like its float32 value."""
+    for layouts ("1x128_t": groups of 128 rows, q [..., cols, rows]).  A
+    bfloat16 source quantizes exactly like its float32 value."""
     bf16 = x.dtype == torch.bfloat16
     _dev(x, torch.bfloat16 if bf16 else torch.float32, "x")
     code = SCALE_KINDS[kind]
@@ -130,9 +133,12 @@ def fp8_quantize(x, kind="1x128", q=None, scales=None):
     for d in lead:
         batch *= d
     if q is None:
-        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        shape = (*lead, cols, rows) if kind == "1x128_t" else x.shape
+        q = torch.empty(shape, dtype=torch.uint8, device=x.device)
     if scales is None:
-        if kind == "1x128":
+        if kind == "1x128_t":
+            scales = torch.empty((*lead, rows // 128, cols), dtype=torch.float32, device=x.device)
+        elif kind == "1x128":
             scales = torch.empty((*lead, cols // 128, rows), dtype=torch.float32, device=x.device)
         elif kind == "128x128":
             scales = torch.empty((*lead, -(-rows // 128), cols // 128), dtype=torch.float32,
@@ -231,6 +237,28 @@ def grouped_gemm_fp8_contiguous_swiglu(a, sa, b, sb, block_expert, q_out=None, s
                                                     _ptr(block_expert), _ptr(q_out), _ptr(s_out),
                                                     m, n, k, E, _stream()))
     return q_out, s_out
+
+
+def grouped_gemm_fp8_kgrouped(a, sa, b, sb, k_offsets, out_dtype=torch.float32, out=None):
+    """Weight-gradient layout: a [m, k_total], sa [k_total/128, m], b [n, k_total],
+    sb [k_total/128, n] (1x128 along K on both), k_offsets int32 [G + 1]
+    (device) -> d [G, m, n] with d[g] = A[:, K_g] B[:, K_g]^T."""
+    _fp8(a, "a"); _fp8(b, "b")
+    _dev(sa, torch.float32, "sa"); _dev(sb, torch.float32, "sb")
+    _dev(k_offsets, torch.int32, "k_offsets")
+    m, k = a.shape
+    n = b.shape[0]
+    G = k_offsets.shape[0] - 1
+    if b.shape != (n, k) or sa.shape != (k // 128, m) or sb.shape != (k // 128, n) or G < 1:
+        raise ValueError("operand shapes disagree")
+    if out is None:
+        out = torch.empty((G, m, n), dtype=out_dtype, device=a.device)
+    _dev(out, out.dtype, "out")
+    if out.shape != (G, m, n):
+        raise ValueError("output shape disagrees")
+    _check(lib().grouped_gemm_fp8_kgrouped(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(k_offsets),
+                                           _ptr(out), _out_code(out.dtype), G, m, n, k, _stream()))
+    return out
 
 
 def grouped_gemm_fp8_masked(a, sa, b, sb, valid_rows, out_dtype=torch.bfloat16, out=None):

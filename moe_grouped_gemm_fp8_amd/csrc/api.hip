@@ -30,6 +30,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // row / column counts must fit int32
 constexpr int64_t kMaxK = 16384;                // sb staging covers 128 K blocks per unit
+constexpr int64_t kMaxKGrouped = ((int64_t)1 << 24) - 128;
 
 fg8_status check_k(const char* fn, int64_t k) {
   if (k < 128 || k > kMaxK) return fail(FG8_EUNSUPPORTED, "%s: k=%lld must be in [128, %lld]", fn,
@@ -40,7 +41,7 @@ fg8_status check_k(const char* fn, int64_t k) {
 
 // The kernels count work units (tiles times splits) in 32-bit integers.
 fg8_status check_units(const fg8::GemmProblem& p, const fg8::TileChoice& t, const char* fn) {
-  const int64_t units = (int64_t)(p.mode == fg8::kMasked ? p.groups : 1) *
+  const int64_t units = (int64_t)(p.mode == fg8::kMasked || p.mode == fg8::kKGrouped ? p.groups : 1) *
                         ((p.M + t.bm - 1) / t.bm) * ((p.N + t.bn - 1) / t.bn) * t.splits;
   if (units >= INT32_MAX)
     return fail(FG8_EUNSUPPORTED, "%s: %lld tiles exceed the 32-bit work-unit count", fn,
@@ -61,7 +62,7 @@ fg8_status run(fg8::GemmProblem& p, const char* fn, hipStream_t stream) {
 
 extern "C" {
 
-int fg8_version(void) { return 400; }   // 0.4.0
+int fg8_version(void) { return 500; }   // 0.5.0
 
 const char* fg8_last_error(void) { return g_err; }
 
@@ -78,15 +79,22 @@ fg8_status quantize_any(const char* fn, const void* x, bool bf16, int64_t batch,
   if (batch < 1 || rows < 1 || cols < 1 || batch >= 65536 || rows >= kMaxDim || cols >= kMaxDim)
     return fail(FG8_EINVAL, "%s: bad sizes batch=%lld rows=%lld cols=%lld", fn, (long long)batch,
                 (long long)rows, (long long)cols);
-  if (kind != FG8_SCALE_1x128 && kind != FG8_SCALE_128x128 && kind != FG8_SCALE_MX1x32)
+  if (kind != FG8_SCALE_1x128 && kind != FG8_SCALE_128x128 && kind != FG8_SCALE_MX1x32 &&
+      kind != FG8_SCALE_1x128_T)
     return fail(FG8_EINVAL, "%s: unknown scale kind %d", fn, (int)kind);
-  const int64_t unit = kind == FG8_SCALE_MX1x32 ? 32 : 128;
+  if (kind == FG8_SCALE_1x128_T) {
+    if (rows % 128 || cols % 64)
+      return fail(FG8_EUNSUPPORTED, "%s: transposed 1x128 needs rows %% 128 == 0 and cols %% 64 == 0"
+                  " (rows=%lld cols=%lld)", fn, (long long)rows, (long long)cols);
+    if (rows / 128 >= 65536) return fail(FG8_EUNSUPPORTED, "%s: too many row blocks", fn);
+  }
+  const int64_t unit = kind == FG8_SCALE_MX1x32 ? 32 : kind == FG8_SCALE_1x128_T ? 64 : 128;
   if (cols % unit)
     return fail(FG8_EUNSUPPORTED, "%s: cols=%lld is not a multiple of %lld", fn, (long long)cols,
                 (long long)unit);
   if (kind == FG8_SCALE_128x128 && (rows + 127) / 128 >= 65536)
     return fail(FG8_EUNSUPPORTED, "%s: too many row blocks", fn);
-  if (kind != FG8_SCALE_MX1x32 && cols / 128 >= 65536)
+  if ((kind == FG8_SCALE_1x128 || kind == FG8_SCALE_128x128) && cols / 128 >= 65536)
     return fail(FG8_EUNSUPPORTED, "%s: too many column blocks", fn);
   const hipError_t e =
       fg8::launch_quantize(x, bf16, batch, rows, cols, (int)kind, q, scales, stream);
@@ -206,6 +214,35 @@ fg8_status grouped_gemm_fp8_contiguous_swiglu(const uint8_t* a, const float* sa,
   p.mode = fg8::kContiguous; p.M = m_total; p.N = n; p.K = k; p.groups = num_experts;
   p.block_expert = block_expert;
   p.swiglu = 1; p.q_out = q_out; p.s_out = s_out;
+  return run(p, fn, stream);
+}
+
+fg8_status grouped_gemm_fp8_kgrouped(const uint8_t* a, const float* sa, const uint8_t* b,
+                                     const float* sb, const int32_t* k_offsets, void* d,
+                                     fg8_out out, int32_t num_groups, int64_t m, int64_t n,
+                                     int64_t k_total, hipStream_t stream) {
+  const char* fn = "grouped_gemm_fp8_kgrouped";
+  FG8_CHECK_PTR(a);
+  FG8_CHECK_PTR(sa);
+  FG8_CHECK_PTR(b);
+  FG8_CHECK_PTR(sb);
+  FG8_CHECK_PTR(k_offsets);
+  FG8_CHECK_PTR(d);
+  if (out != FG8_OUT_F32 && out != FG8_OUT_BF16) return fail(FG8_EINVAL, "%s: bad out", fn);
+  if (num_groups < 1 || num_groups > 65536)
+    return fail(FG8_EINVAL, "%s: num_groups=%d must be in [1, 65536]", fn, (int)num_groups);
+  if (m < 1 || n < 1 || m >= kMaxDim || n >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: bad sizes m=%lld n=%lld", fn, (long long)m, (long long)n);
+  // K is the whole token axis here: 32-bit LDS-DMA offsets of a 256-row tile
+  // bound it to below 2^24
+  if (k_total < 128 || k_total % 128 || k_total > kMaxKGrouped)
+    return fail(FG8_EUNSUPPORTED, "%s: k_total=%lld must be a multiple of 128 in [128, %lld]", fn,
+                (long long)k_total, (long long)kMaxKGrouped);
+  fg8::GemmProblem p{};
+  p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.d = d;
+  p.out_bf16 = out == FG8_OUT_BF16;
+  p.mode = fg8::kKGrouped; p.M = m; p.N = n; p.K = k_total; p.groups = num_groups;
+  p.k_offsets = k_offsets;
   return run(p, fn, stream);
 }
 

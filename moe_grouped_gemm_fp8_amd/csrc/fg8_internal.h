@@ -6,7 +6,10 @@
 
 namespace fg8 {
 
-enum GemmMode : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+// kKGrouped: per group g, the K range k_offsets[g] .. k_offsets[g+1] of
+// shared A [M][K] and B [N][K], both with 1x128 scales ([K/128][M] and
+// [K/128][N]); D [G][M][N].
+enum GemmMode : int { kDense = 0, kContiguous = 1, kMasked = 2, kKGrouped = 3 };
 
 // One GEMM problem as the kernels see it.  Per group g (expert or batch
 // entry): A rows [M][K], B [N][K], D [M][N].  Scales are FP32 (block-scaled
@@ -24,6 +27,7 @@ struct GemmProblem {
   int groups;                   // experts (masked / contiguous) or 1
   const int32_t* block_expert;  // contiguous: expert of each 128-row block
   const int32_t* valid;         // masked: live rows per group (NULL = all M)
+  const int32_t* k_offsets;     // K-grouped: K offset of each group [groups + 1]
   int rotate;                   // 1: start each unit's K walk at a unit-dependent block
   // contiguous only: 1 = fused SiLU-gated epilogue that writes the 1x128
   // quantization of h = silu(gate) * up (W1 rows interleaved in 128-row

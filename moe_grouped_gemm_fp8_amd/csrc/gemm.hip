@@ -230,6 +230,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
     if (tid == C::THREADS - 1) tile_prefix[G] = run;   // grand total (G <= 1024)
     __syncthreads();
     total = tile_prefix[G];
+  } else if constexpr (MODE == kKGrouped) {
+    total = p.groups * (int)((M + C::BM - 1) / C::BM) * n_tiles;
   } else {
     total = (int)((M + C::BM - 1) / C::BM) * n_tiles * splits;
   }
@@ -252,6 +254,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       w.n0 = (int64_t)(t % n_tiles) * C::BN;
       w.kb0 = 0; w.kb1 = KB; w.split = 0; w.tile = u;
       w.rows = p.valid ? (int)min(max((int64_t)p.valid[lo], (int64_t)0), M) : (int)M;
+    } else if constexpr (MODE == kKGrouped) {
+      const int per = (int)((M + C::BM - 1) / C::BM) * n_tiles;
+      w.g = u / per;
+      const int t = u - w.g * per;
+      w.m0 = (int64_t)(t / n_tiles) * C::BM;
+      w.n0 = (int64_t)(t % n_tiles) * C::BN;
+      // the group's K blocks, range-checked: [k0, k1) inside [0, KB)
+      const int k0 = min(max(p.k_offsets[w.g] / kGroup, 0), KB);
+      const int k1 = min(max(p.k_offsets[w.g + 1] / kGroup, k0), KB);
+      w.kb0 = k0; w.kb1 = k1; w.split = 0; w.tile = u;
+      w.rows = (int)M;
     } else {
       const int t = u / splits;
       w.split = u % splits;
@@ -289,6 +302,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
         gsa = (const float*)p.sa + (int64_t)w.g * KB * M;
         gsb = (const float*)p.sb + (int64_t)w.g * nb_blocks * KB;
       }
+    } else if constexpr (MODE == kKGrouped) {
+      ga = p.a;
+      gsa = (const float*)p.sa;
+      gsb = (const float*)p.sb;   // [KB][N]: one scale per B row and K block
     } else {
       ga = p.a;
       gb = p.b + (int64_t)w.g * N * K;
@@ -331,12 +348,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       if constexpr (MX) {
         const int64_t rb = w.n0 + wave * C::B_ROWS + lane;
         sb_off = (uint32_t)(((rb < N - 1 ? rb : N - 1) - w.n0) * (K / kMxBlock));
+      } else if constexpr (MODE == kKGrouped) {
+        const int64_t rb = w.n0 + wave * C::B_ROWS + lane;
+        sb_off = (uint32_t)(((rb < N - 1 ? rb : N - 1) - w.n0) * 4);
       }
     }
     // the B-block scale row of this wave's columns (FP32 path)
     const int64_t nbw0 = (w.n0 + wn0) / kGroup;
     const int64_t nbw = nbw0 < nb_blocks - 1 ? nbw0 : nb_blocks - 1;
-    const float* sb_row = MX ? nullptr : gsb + nbw * KB;
+    const float* sb_row = MX || MODE == kKGrouped ? nullptr : gsb + nbw * KB;
     const uint8_t* a_tile = ga + w.m0 * K;
     const uint8_t* b_tile = gb + w.n0 * K;
     // One LDS-DMA instruction of K block kb into block slot `sub` of stage
@@ -372,6 +392,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
           const uint8_t* ebb = uniform(geb + w.n0 * (K / kMxBlock) + kb * 4);
           const uint32_t lb = uniform(sst + (uint32_t)(C::SA_BYTES + wave * C::B_ROWS * 4));
           if (lane < C::B_ROWS) dma4(ebb, sb_off, lb);
+        } else if constexpr (MODE == kKGrouped) {
+          // the B row scales of K block kb: one FP32 per row
+          const float* sbb = uniform(gsb + (int64_t)kb * N + w.n0);
+          const uint32_t lb = uniform(sst + (uint32_t)(C::SA_BYTES + wave * C::B_ROWS * 4));
+          if (lane < C::B_ROWS) dma4(sbb, sb_off, lb);
         } else {
           // this wave's B-block scale for K block kb, one lane
           const float* sbp = uniform(sb_row + kb);
@@ -396,7 +421,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
     // tiles that run at the same time and share an operand (the A rows of a
     // skinny GEMM, the A tile of a row of output tiles) then read different
     // K blocks of it instead of all hitting the same L2 lines at once.
-    const int rot = p.rotate ? uniform(u % nkb) : 0;
+    const int rot = p.rotate && nkb > 0 ? uniform(u % nkb) : 0;
     auto kb_of = [&](int j) {
       const int x = j + rot;
       return w.kb0 + (x >= nkb ? x - nkb : x);
@@ -466,8 +491,18 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
             issue_point(sub * C::TN + tn);
           }
         } else {
+          // one B scale per wave (128-row blocks of B), or one per B row
+          // (K-grouped: 1x128 scales on both operands, applied per column)
           const float sbv =
-              *reinterpret_cast<const float*>(Ss + C::SA_BYTES + C::SB_BYTES + wave * 4);
+              MODE == kKGrouped
+                  ? 1.f
+                  : *reinterpret_cast<const float*>(Ss + C::SA_BYTES + C::SB_BYTES + wave * 4);
+          float sbc[C::TN];
+#pragma unroll
+          for (int tn = 0; tn < C::TN; ++tn)
+            sbc[tn] = MODE == kKGrouped ? reinterpret_cast<const float*>(Ss + C::SA_BYTES)
+                                              [wn0 + tn * 16 + (lane & 15)]
+                                        : 1.f;
           v4f sc[C::TM];
 #pragma unroll
           for (int tm = 0; tm < C::TM; ++tm) {
@@ -495,18 +530,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
 #pragma unroll
               for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
-                for (int v = 0; v < 4; ++v)
-                  acc[tm][tn - 1][v] =
-                      fmaf(part[(tn - 1) & 1][tm][v], sc[tm][v], acc[tm][tn - 1][v]);
+                for (int v = 0; v < 4; ++v) {
+                  const float f = MODE == kKGrouped ? sc[tm][v] * sbc[tn - 1] : sc[tm][v];
+                  acc[tm][tn - 1][v] = fmaf(part[(tn - 1) & 1][tm][v], f, acc[tm][tn - 1][v]);
+                }
             }
             issue_point(sub * C::TN + tn);
           }
 #pragma unroll
           for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
+            for (int v = 0; v < 4; ++v) {
+              const float f = MODE == kKGrouped ? sc[tm][v] * sbc[C::TN - 1] : sc[tm][v];
               acc[tm][C::TN - 1][v] =
-                  fmaf(part[(C::TN - 1) & 1][tm][v], sc[tm][v], acc[tm][C::TN - 1][v]);
+                  fmaf(part[(C::TN - 1) & 1][tm][v], f, acc[tm][C::TN - 1][v]);
+            }
         }
       }
     }
@@ -621,7 +659,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       constexpr int FIT = C::STAGES * C::STAGE_BYTES / ROW;
       constexpr int CR = FIT >= C::BM ? C::BM : (FIT / C::WM) * C::WM;
       static_assert(CR >= C::WM && C::BM % CR == 0, "output rows must stage in whole wave blocks");
-      const int64_t d_off = MODE == kMasked ? (int64_t)w.g * M * N : 0;
+      const int64_t d_off = MODE == kMasked || MODE == kKGrouped ? (int64_t)w.g * M * N : 0;
       const bool vec = (N * ESZ) % 16 == 0;   // every row starts 16-byte aligned
 #pragma unroll
       for (int r0 = 0; r0 < C::BM; r0 += CR) {
@@ -754,6 +792,8 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
     t.cfg = ov;
   } else if (p.mode == kContiguous) {
     t.cfg = kCfgWide8;
+  } else if (p.mode == kKGrouped) {
+    t.cfg = kCfgBig8;
   } else if (p.mode == kDense && (forced = tile_override(&t.cfg, &forced_splits))) {
   } else if (p.mode == kDense && p.M <= 64) {
     // decode-sized M: narrow 64 x 32 tiles (four K blocks per stage) split
@@ -772,8 +812,8 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
   const int64_t KB = p.K / kGroup;
   int64_t units;
   t.splits = 1;
-  if (p.mode == kMasked) {
-    units = (int64_t)p.groups * ((p.M + t.bm - 1) / t.bm) * n_tiles;   // upper bound
+  if (p.mode == kMasked || p.mode == kKGrouped) {
+    units = (int64_t)p.groups * ((p.M + t.bm - 1) / t.bm) * n_tiles;   // masked: upper bound
   } else {
     const int64_t tiles = ((p.M + t.bm - 1) / t.bm) * n_tiles;
     if (p.mode == kDense && kCfgs[t.cfg].splitk) {
@@ -836,6 +876,8 @@ hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
       if (p.mx) return launch<CfgWide8, true, kContiguous>(p, t.grid, s);
       if (t.cfg == kCfgWide8) return launch<CfgWide8, false, kContiguous>(p, t.grid, s);
       return launch<CfgWide, false, kContiguous>(p, t.grid, s);
+    case kKGrouped:
+      return launch<CfgBig8, false, kKGrouped>(p, t.grid, s);
     default:
       if (t.cfg == kCfgBig8) {
         if (p.mx) return launch<CfgBig8, true, kMasked>(p, t.grid, s);

@@ -150,6 +150,70 @@ static hipError_t launch_q1(const T* x, const int32_t* row_src, int64_t rows_all
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------- 1 x 128, transposed
+// Groups of 128 consecutive ROWS of each column (the token axis of an
+// activation), codes written transposed: q[c][r], scales [rows/128][cols].
+// A workgroup takes a 128-row x 64-column tile: thread t loads rows
+// 8 (t / 16) .. +7 of columns 4 (t % 16) .. +3 as float4 / 8-byte BF16 rows
+// (coalesced along the row), the 16 row parts of a column meet in LDS for the
+// amax, and the codes are transposed through LDS so that every column's 128
+// codes leave as whole 128-byte lines.
+template <class T>
+__global__ __launch_bounds__(256) void quant_1x128_t_kernel(const T* __restrict__ x,
+                                                            uint8_t* __restrict__ q,
+                                                            float* __restrict__ s, int64_t rows,
+                                                            int64_t cols) {
+  __shared__ float part[16][64];
+  __shared__ float col_scale[64];
+  __shared__ uint32_t codes[64][33];   // 64 columns x 32 dwords of codes, padded
+  const int64_t b = blockIdx.z;
+  const int64_t rb = blockIdx.y;
+  const int64_t c_tile = (int64_t)blockIdx.x * 64;
+  const int t = threadIdx.x, cq = t & 15, rp = t >> 4;
+  const T* xb = x + b * rows * cols;
+  const int64_t r0 = rb * kGroup + rp * 8;
+  float4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = load4(xb + (r0 + i) * cols + c_tile + cq * 4);
+  float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    m.x = fmaxf(m.x, fabsf(v[i].x)); m.y = fmaxf(m.y, fabsf(v[i].y));
+    m.z = fmaxf(m.z, fabsf(v[i].z)); m.w = fmaxf(m.w, fabsf(v[i].w));
+  }
+  *reinterpret_cast<float4*>(&part[rp][cq * 4]) = m;
+  __syncthreads();
+  if (t < 64) {
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, part[j][t]);
+    const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
+    col_scale[t] = sc;
+    s[b * (rows / kGroup) * cols + rb * cols + c_tile + t] = sc;
+  }
+  __syncthreads();
+  const float4 sc4 = *reinterpret_cast<const float4*>(&col_scale[cq * 4]);
+  const float scj[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 w = v[i];
+      e[i] = (j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w) / scj[j];
+    }
+    codes[cq * 4 + j][rp * 2] = pack4_e4m3(make_float4(e[0], e[1], e[2], e[3]));
+    codes[cq * 4 + j][rp * 2 + 1] = pack4_e4m3(make_float4(e[4], e[5], e[6], e[7]));
+  }
+  __syncthreads();
+  // column cc = t / 4 of the tile, 32-byte piece t % 4 of its 128 codes
+  const int cc = t >> 2, piece = t & 3;
+  uint8_t* dst = q + b * cols * rows + (c_tile + cc) * rows + rb * kGroup + piece * 32;
+  const uint32_t* src = &codes[cc][piece * 8];
+  *reinterpret_cast<uint4*>(dst) = make_uint4(src[0], src[1], src[2], src[3]);
+  *reinterpret_cast<uint4*>(dst + 16) = make_uint4(src[4], src[5], src[6], src[7]);
+}
+
 // ---------------------------------------------------------------- 128 x 128
 // Block: 256 threads over one 128x128 block.  Thread t owns column chunk
 // (t % 32) * 4 of rows t / 32 + 8 i, i = 0..15: 16 float4 in registers, the
@@ -226,6 +290,10 @@ static hipError_t launch_quantize_t(const T* x, int64_t batch, int64_t rows, int
   } else if (kind == 1) {
     dim3 grid((unsigned)(cols / kGroup), (unsigned)((rows + kGroup - 1) / kGroup), (unsigned)batch);
     hipLaunchKernelGGL(quant_128x128_kernel<T>, grid, dim3(256), 0, stream, x, q, (float*)scales,
+                       rows, cols);
+  } else if (kind == 3) {
+    dim3 grid((unsigned)(cols / 64), (unsigned)(rows / kGroup), (unsigned)batch);
+    hipLaunchKernelGGL(quant_1x128_t_kernel<T>, grid, dim3(256), 0, stream, x, q, (float*)scales,
                        rows, cols);
   } else {
     const int64_t nblocks = batch * rows * cols / kMxBlock;

@@ -185,3 +185,20 @@ def check_swiglu_quant(q, s, C, S, F, K, where=""):
     ok = (dq >= lo) & (dq <= hi)
     assert ok.all(), f"{where}: {np.count_nonzero(~ok)} of {ok.size} codes outside their bounds"
     return int(np.count_nonzero(dq != e4m3.round_to_e4m3_value(np.float32(h / sf))))
+
+
+def ref_kgrouped(qa, sa, qb, sb, offsets):
+    """Oracle (C, S, S_trunc) [G, M, N] of the K-grouped GEMM (1x128 scales
+    on both operands)."""
+    from oracle import backward
+    C, S = backward.grouped_k(qa, sa, qb, sb, offsets)
+    F = np.zeros_like(C)
+    sa64, sb64 = np.abs(np.asarray(sa, np.float64)), np.abs(np.asarray(sb, np.float64))
+    off = np.asarray(offsets, np.int64)
+    for g in range(off.size - 1):
+        k0, k1 = int(off[g]), int(off[g + 1])
+        if k1 > k0:
+            b0 = k0 // 128
+            scale = lambda m, n, gi, b0=b0: sa64[b0 + gi // 8, m] * sb64[b0 + gi // 8, n]
+            F[g] = trunc_bound(np.asarray(qa)[:, k0:k1], np.asarray(qb)[:, k0:k1], scale)
+    return C, S, F

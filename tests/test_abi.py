@@ -32,14 +32,15 @@ def test_header_lists_the_five_entry_points():
               "grouped_gemm_fp8_masked", "gemm_mxfp8", "fg8_gemm_workspace_bytes",
               "fg8_last_error", "fg8_version", "fp8_quantize_bf16",
               "grouped_gemm_mxfp8_contiguous", "moe_contiguous_layout_fp8",
-              "fg8_moe_capacity", "grouped_gemm_fp8_contiguous_swiglu"):
+              "fg8_moe_capacity", "grouped_gemm_fp8_contiguous_swiglu",
+              "grouped_gemm_fp8_kgrouped"):
         assert n in names
 
 
 def test_every_declared_symbol_is_exported(L):
     for n in _declared():
         assert hasattr(L, n), f"{n} declared in fg8.h but not exported"
-    assert L.fg8_version() == 400
+    assert L.fg8_version() == 500
 
 
 P = ctypes.c_void_p
@@ -160,3 +161,21 @@ def test_swiglu_validation(L):
     assert f(ok, ok, ok, ok, ok, ok, ok, 200, 512, 512, 4, None) == 2      # m_total % 128
     assert f(ok, ok, ok, ok, ok, ok, ok, 256, 512, 500, 4, None) == 2      # k % 128
     assert f(ok, ok, ok, ok, ok, ok, ok, 256, 512, 512, 0, None) == 1
+
+
+def test_kgrouped_and_transposed_quantize_validation(L):
+    ok = _fake(0x10000)
+    f = L.grouped_gemm_fp8_kgrouped
+    f.argtypes = [P] * 6 + [ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64,
+                            ctypes.c_int64, P]
+    assert f(ok, ok, ok, ok, None, ok, 0, 4, 256, 512, 1024, None) == 1
+    assert b"k_offsets is NULL" in L.fg8_last_error()
+    assert f(ok, ok, ok, ok, ok, ok, 0, 0, 256, 512, 1024, None) == 1
+    assert f(ok, ok, ok, ok, ok, ok, 0, 4, 256, 512, 1000, None) == 2
+    assert f(ok, ok, ok, ok, ok, ok, 0, 4, 256, 512, 1 << 24, None) == 2
+    assert f(ok, ok, ok, ok, ok, ok, 3, 4, 256, 512, 1024, None) == 1
+    q = L.fp8_quantize
+    assert q(ok, 1, 200, 128, 3, ok, ok, None) == 2          # rows not whole groups
+    assert b"transposed" in L.fg8_last_error()
+    assert q(ok, 1, 256, 96, 3, ok, ok, None) == 2           # cols % 64
+    assert q(ok, 1, 256, 4, 4, ok, ok, None) == 1            # unknown kind

@@ -1,0 +1,125 @@
+"""Training-backward pieces on the GPU against the oracle (oracle/backward.py):
+the 1x128 quantization along the token axis with transposed codes
+(bit-exact), and the K-grouped weight-gradient GEMM (FP32 / BF16 bars of
+tests/parity.py)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_grouped_gemm_fp8_amd as fg8
+from moe_grouped_gemm_fp8_amd import inputs
+from oracle import backward, routing
+from parity import check_bf16, check_f32, ref_kgrouped
+from test_gpu_quantize import _hard_values
+
+pytestmark = pytest.mark.gpu
+
+
+def _to_bf16(x):
+    u = x.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return r, (r.astype(np.uint32) << 16).view(np.float32)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("shape", [(1, 128, 64), (2, 384, 192), (1, 1024, 7168)])
+def test_transposed_quantize_bit_exact(dev, shape, bf16):
+    batch, rows, cols = shape
+    g = np.random.default_rng(300 + rows)
+    x = np.stack([_hard_values(g, (cols, rows)).T for _ in range(batch)])   # groups down columns
+    print(f"transposed quantize {shape} bf16={bf16}", flush=True)
+    if bf16:
+        bits, x = _to_bf16(np.ascontiguousarray(x))
+        t = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    q, s = fg8.fp8_quantize(t, "1x128_t")
+    torch.cuda.synchronize()
+    q, s = q.cpu().numpy(), s.cpu().numpy()
+    assert q.shape == (batch, cols, rows) and s.shape == (batch, rows // 128, cols)
+    for b in range(batch):
+        qo, so = backward.quantize_1x128_transposed(x[b])
+        assert np.array_equal(q[b], qo)
+        assert np.array_equal(s[b].view(np.uint32), so.view(np.uint32))
+
+
+def _operands(T, m, n, seed):
+    g = np.random.default_rng(seed)
+    dy = (g.standard_normal((T, m)) * np.exp(g.uniform(-3, 3, (T, 1)))).astype(np.float32)
+    x = g.standard_normal((T, n)).astype(np.float32)
+    qa, sa = backward.quantize_1x128_transposed(dy)
+    qb, sb = backward.quantize_1x128_transposed(x)
+    return qa, sa, qb, sb
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("case", [
+    (300, 200, [0, 256, 256, 1024, 1152]),          # an empty group, ragged m and n
+    (256, 384, [0, 128]),                            # one single-block group
+    (64, 130, [0, 512, 1536, 1536, 1536, 2048]),    # trailing empty groups
+])
+def test_kgrouped_small(dev, case, out_dtype):
+    m, n, off = case
+    T = off[-1]
+    qa, sa, qb, sb = _operands(T, m, n, 310 + m)
+    print(f"kgrouped m={m} n={n} offsets={off} out={out_dtype}", flush=True)
+    ta, tsa, tb, tsb = [torch.from_numpy(np.ascontiguousarray(v)).cuda() for v in (qa, sa, qb, sb)]
+    toff = torch.tensor(off, dtype=torch.int32, device="cuda")
+    d = torch.full((len(off) - 1, m, n), float("nan"), dtype=out_dtype, device="cuda")
+    fg8.grouped_gemm_fp8_kgrouped(ta, tsa, tb, tsb, toff, out=d)
+    torch.cuda.synchronize()
+    C, S, F = ref_kgrouped(qa, sa, qb, sb, off)
+    for g in range(len(off) - 1):
+        where = f"group {g} K [{off[g]}, {off[g + 1]})"
+        if out_dtype == torch.float32:
+            got = d[g].cpu().numpy()
+            if off[g] == off[g + 1]:
+                assert np.all(got == 0.0), where
+            check_f32(got, C[g], S[g], max(off[g + 1] - off[g], 128), where, S_flush=F[g])
+        else:
+            bits = d[g].view(torch.int16).cpu().numpy().view(np.uint16)
+            check_bf16(bits, C[g], S[g], max(off[g + 1] - off[g], 128), where, S_flush=F[g])
+
+
+def test_wgrad_from_the_routing_layout_full_size_sampled(dev):
+    """The weight gradient of W1 for the MoE workload (8192 tokens, top-8 of
+    32 experts, Zipf 1.1): dY [M_pad, 4096] and X [M_pad, 7168] in the
+    contiguous layout (padding rows zero), both quantized along the token
+    axis on the GPU, then the K-grouped GEMM over the routing layout's expert
+    offsets.  The oracle quantizes the sampled columns itself and checks
+    sampled 128 x 128 output blocks of sampled experts."""
+    c = inputs.ContiguousCase()
+    ids = inputs.zipf_topk_routing(c.workload, c.tokens, c.experts, c.topk)
+    m_cap = routing.capacity(c.tokens, c.topk, c.experts)
+    rt, be, off, cnt = routing.contiguous_layout(ids, c.experts, m_cap)
+    M = int(off[-1])                                    # rows in use
+    g = inputs.rng(c.workload, 6)
+    dy = g.standard_normal((M, c.inter), dtype=np.float32)
+    x = inputs.rng(c.workload, 0).standard_normal((c.tokens, c.hidden), dtype=np.float32)
+    X = np.zeros((M, c.hidden), np.float32)
+    live = rt[:M] >= 0
+    X[live] = x[rt[:M][live]]
+    dy[~live] = 0.0
+    del x
+    tdy = torch.from_numpy(dy).cuda()
+    tX = torch.from_numpy(X).cuda()
+    qa, sa = fg8.fp8_quantize(tdy, "1x128_t")
+    qb, sb = fg8.fp8_quantize(tX, "1x128_t")
+    del tdy, tX
+    toff = torch.from_numpy(off.astype(np.int32)).cuda()
+    d = fg8.grouped_gemm_fp8_kgrouped(qa, sa, qb, sb, toff, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    gs = np.random.default_rng(406)
+    for e in gs.choice(c.experts, 6, replace=False):
+        k0, k1 = int(off[e]), int(off[e + 1])
+        if k1 == k0:
+            continue
+        ib = gs.integers(0, c.inter // 128)
+        jb = gs.integers(0, c.hidden // 128)
+        rows = np.arange(ib * 128, ib * 128 + 128)
+        cols = np.arange(jb * 128, jb * 128 + 128)
+        qa_o, sa_o = backward.quantize_1x128_transposed(dy[k0:k1, rows])
+        qb_o, sb_o = backward.quantize_1x128_transposed(X[k0:k1, cols])
+        C, S, F = ref_kgrouped(qa_o, sa_o, qb_o, sb_o, [0, k1 - k0])
+        got = d[e, ib * 128:(ib + 1) * 128, jb * 128:(jb + 1) * 128].cpu().numpy()
+        check_f32(got, C[0], S[0], k1 - k0, f"expert {e} block ({ib}, {jb})", S_flush=F[0])
