@@ -219,8 +219,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": measured_traffic(),
-                "kernel": "fg8::gemm_kernel, 64x32 tiles, 4 K blocks per stage, split-K "
-                          "(64x2112x7168, BF16 out)",
+                "kernel": "fg8::gemm_kernel, 64x32 tiles, two workgroups per CU, 2 K blocks "
+                          "per stage, 7-way split-K (64x2112x7168, BF16 out)",
                 "algorithmic_bytes": algo, "avg_us": round(avg_ms * 1e3, 3),
                 "timing": "HIP events around back-to-back graph launches on the kernel's stream",
                 "single_launch_us": {"avg": round(ev_avg * 1e3, 3), "median": round(ev_med * 1e3, 3),

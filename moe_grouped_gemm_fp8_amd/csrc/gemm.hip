@@ -724,6 +724,7 @@ using CfgS64k4 = Cfg<64, 64, 1, 4, 2, 1, 4>;   // 64 x 16
 using CfgS64k2 = Cfg<64, 64, 1, 4, 4, 1, 2>;   // 64 x 16
 using CfgS128k2 = Cfg<64, 128, 1, 4, 3, 1, 2>; // 64 x 32
 using CfgM32k2 = Cfg<128, 32, 4, 1, 3, 1, 2>;  // 32 x 32
+using CfgS32x2k2 = Cfg<64, 32, 2, 2, 3, 2, 2>; // 32 x 16, two workgroups per CU
 
 struct CfgInfo {
   int bm, bn, occ;
@@ -735,11 +736,13 @@ static const CfgInfo kCfgs[] = {
     FG8_CFG_INFO(CfgS64),  FG8_CFG_INFO(CfgS128), FG8_CFG_INFO(CfgM64),  FG8_CFG_INFO(CfgM32),
     FG8_CFG_INFO(CfgBig8), FG8_CFG_INFO(CfgWide8), FG8_CFG_INFO(CfgS32k4), FG8_CFG_INFO(CfgS32k2),
     FG8_CFG_INFO(CfgS64k4), FG8_CFG_INFO(CfgS64k2), FG8_CFG_INFO(CfgS128k2), FG8_CFG_INFO(CfgM32k2),
+    FG8_CFG_INFO(CfgS32x2k2),
 };
 #undef FG8_CFG_INFO
 enum CfgId {
   kCfgBig = 0, kCfgWide, kCfgS32, kCfgS32x2, kCfgS64, kCfgS128, kCfgM64, kCfgM32, kCfgBig8,
-  kCfgWide8, kCfgS32k4, kCfgS32k2, kCfgS64k4, kCfgS64k2, kCfgS128k2, kCfgM32k2, kNumCfgs
+  kCfgWide8, kCfgS32k4, kCfgS32k2, kCfgS64k4, kCfgS64k2, kCfgS128k2, kCfgM32k2, kCfgS32x2k2,
+  kNumCfgs
 };
 
 int device_cu_count() {
@@ -796,10 +799,11 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
     t.cfg = kCfgBig8;
   } else if (p.mode == kDense && (forced = tile_override(&t.cfg, &forced_splits))) {
   } else if (p.mode == kDense && p.M <= 64) {
-    // decode-sized M: narrow 64 x 32 tiles (four K blocks per stage) split
-    // along K, unless N alone gives two waves of them, then wider 64 x 128
-    // tiles without a split
-    t.cfg = (p.N + 31) / 32 >= 2 * num_cus ? kCfgS128 : kCfgS32k4;
+    // decode-sized M: narrow 64 x 32 tiles, two workgroups per CU (the
+    // LDS-DMA rate of a CU grows with the waves issuing), two K blocks per
+    // stage, split along K; when N alone gives two waves of them, wider
+    // 64 x 128 tiles without a split
+    t.cfg = (p.N + 31) / 32 >= 2 * num_cus ? kCfgS128 : kCfgS32x2k2;
   } else if (p.mode == kDense && p.M <= 128) {
     t.cfg = kCfgS64k2;
   } else {
@@ -870,6 +874,7 @@ hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
         case kCfgS64k2: return launch<CfgS64k2, false, kDense>(p, t.grid, s);
         case kCfgS128k2: return launch<CfgS128k2, false, kDense>(p, t.grid, s);
         case kCfgM32k2: return launch<CfgM32k2, false, kDense>(p, t.grid, s);
+        case kCfgS32x2k2: return launch<CfgS32x2k2, false, kDense>(p, t.grid, s);
         default: return launch<CfgBig, false, kDense>(p, t.grid, s);
       }
     case kContiguous:
