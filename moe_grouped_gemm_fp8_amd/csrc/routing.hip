@@ -6,11 +6,14 @@
 // expert, each run padded to a multiple of the 128-row M block, and names the
 // expert of every block.  Here it is built on the device from the router's
 // top-k expert ids, so the counts never visit the host:
-//   1. count: one workgroup per expert counts the tokens that chose it;
-//   2. offsets: one workgroup turns the padded counts into run offsets and
-//      labels every 128-row block with its expert (-1 past the last run);
-//   3. place: one workgroup per expert walks the tokens in ascending order
-//      (a block-wide scan gives each token its rank) and writes row_token;
+//   1. count: one workgroup per (expert, token range) counts the tokens of
+//      the range that chose the expert;
+//   2. offsets: one workgroup sums the ranges, turns the padded counts into
+//      run offsets, labels every 128-row block with its expert (-1 past the
+//      last run) and gives every (expert, range) its first row;
+//   3. place: one workgroup per (expert, token range) walks its tokens in
+//      ascending order (a block-wide scan gives each token its rank) and
+//      writes row_token;
 //   4. gather + quantize: 1x128 groups of the source row of every layout row
 //      (zeros, scale 1, for padding), as the 1x128 quantizer does.
 // Steps 1-3 read only the ids (tokens x top-k int32); step 4 is the HBM
@@ -23,14 +26,50 @@ namespace fg8 {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 
-// Does token t route to expert e?  A repeated id counts once; ids outside
-// [0, E) route nowhere.
-__device__ __forceinline__ int routes_to(const int32_t* __restrict__ ids, int64_t t, int topk,
-                                         int e) {
-  int hit = 0;
-  for (int j = 0; j < topk; ++j) hit |= ids[t * topk + j] == e;
-  return hit;
-}
+// The ids are walked in chunks of up to kChunkInts ids.  A chunk is loaded
+// into registers (kIdsPerThread coalesced loads per thread, all in flight,
+// issued while the previous chunk is being examined) and stored to LDS
+// id-major: id j of chunk token t at lds[j * (ct + 1) + t], so the threads of
+// a wave, which examine consecutive tokens, read consecutive words (the odd
+// stride keeps the stores nearly conflict-free too).  Tokens are examined in
+// rounds of kRouteThreads consecutive tokens, thread i taking token i of the
+// round.
+constexpr int kIdsPerThread = 8;
+constexpr int kChunkInts = kRouteThreads * kIdsPerThread;   // 32 KB of ids
+constexpr int kChunkLds = kChunkInts + 256;                 // + the odd-stride padding
+constexpr int kMaxRouteSplits = 64;
+
+struct IdChunks {
+  const int32_t* ids;
+  int64_t tokens;         // end of this workgroup's token range
+  int topk, ct, stride;   // tokens per chunk, LDS stride
+  __device__ IdChunks(const int32_t* i, int64_t end, int k)
+      : ids(i), tokens(end), topk(k), ct(kChunkInts / k), stride(kChunkInts / k + 1) {}
+  __device__ int64_t count(int64_t t0) const { return tokens - t0 < ct ? tokens - t0 : ct; }
+  __device__ void load(int64_t t0, int32_t (&v)[kIdsPerThread]) const {
+    const int64_t n = count(t0) * topk;
+#pragma unroll
+    for (int i = 0; i < kIdsPerThread; ++i) {
+      const int64_t j = (int64_t)i * kRouteThreads + threadIdx.x;
+      v[i] = j < n ? ids[t0 * topk + j] : -1;
+    }
+  }
+  __device__ void store(const int32_t (&v)[kIdsPerThread], int32_t* lds) const {
+#pragma unroll
+    for (int i = 0; i < kIdsPerThread; ++i) {
+      const int g = i * kRouteThreads + threadIdx.x;   // id g = token * topk + j of the chunk
+      const int t = g / topk, j = g - t * topk;
+      if (t < ct) lds[j * stride + t] = v[i];
+    }
+  }
+  // Does chunk token t route to expert e?  A repeated id counts once; ids
+  // outside [0, E) route nowhere.
+  __device__ int hit(const int32_t* lds, int t, int e) const {
+    int h = 0;
+    for (int j = 0; j < topk; ++j) h |= lds[j * stride + t] == e;
+    return h;
+  }
+};
 
 // Block-wide exclusive scan of one int per thread; also returns the total.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* total) {
@@ -56,23 +95,53 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total) {
   return base + incl - v;
 }
 
+// The token axis is cut into `splits` ranges of tokens_per_split tokens;
+// workgroup (e, s) examines range s for expert e, so that every range is about
+// one chunk.  The per-range counts go to split_counts[e * splits + s].
 __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(
-    const int32_t* __restrict__ ids, int64_t tokens, int topk, int32_t* __restrict__ counts) {
-  const int e = blockIdx.x;
+    const int32_t* __restrict__ ids, int64_t tokens, int topk, int64_t tokens_per_split,
+    int32_t* __restrict__ split_counts) {
+  __shared__ int32_t chunk[kChunkLds];
+  const int e = blockIdx.x, sp = blockIdx.y;
+  const int64_t first = (int64_t)sp * tokens_per_split;
+  const int64_t last = first + tokens_per_split < tokens ? first + tokens_per_split : tokens;
+  const IdChunks ch(ids, last, topk);
+  int32_t v[kIdsPerThread];
+  if (first < last) ch.load(first, v);
   int n = 0;
-  for (int64_t t = threadIdx.x; t < tokens; t += kRouteThreads) n += routes_to(ids, t, topk, e);
+  for (int64_t t0 = first; t0 < last; t0 += ch.ct) {
+    __syncthreads();   // the previous chunk has been examined
+    ch.store(v, chunk);
+    __syncthreads();
+    if (t0 + ch.ct < last) ch.load(t0 + ch.ct, v);   // in flight meanwhile
+    const int64_t nt = ch.count(t0);
+    for (int t = threadIdx.x; t < nt; t += kRouteThreads) n += ch.hit(chunk, t, e);
+  }
   int total;
   block_exclusive_scan(n, &total);
-  if (threadIdx.x == 0) counts[e] = total;
+  if (threadIdx.x == 0) split_counts[(int64_t)e * gridDim.y + sp] = total;
 }
 
-// One workgroup; num_experts <= kRouteThreads.
+// One workgroup; num_experts <= kRouteThreads.  Sums the range counts of
+// each expert into counts[e], turns them into exclusive prefixes in place
+// (the first row of each range's tokens inside the expert's run), and lays
+// the runs out.
 __global__ __launch_bounds__(kRouteThreads) void route_offsets_kernel(
-    const int32_t* __restrict__ counts, int num_experts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ block_expert, int64_t nblocks) {
+    int32_t* __restrict__ split_counts, int splits, int32_t* __restrict__ counts,
+    int num_experts, int32_t* __restrict__ offsets, int32_t* __restrict__ block_expert,
+    int64_t nblocks) {
   __shared__ int off[kRouteThreads + 1];
   const int e = threadIdx.x;
-  const int padded = e < num_experts ? (counts[e] + kGroup - 1) / kGroup * kGroup : 0;
+  int cnt = 0;
+  if (e < num_experts) {
+    for (int sp = 0; sp < splits; ++sp) {
+      const int c = split_counts[e * splits + sp];
+      split_counts[e * splits + sp] = cnt;
+      cnt += c;
+    }
+    counts[e] = cnt;
+  }
+  const int padded = e < num_experts ? (cnt + kGroup - 1) / kGroup * kGroup : 0;
   int total;
   const int start = block_exclusive_scan(padded, &total);
   if (e < num_experts) {
@@ -95,42 +164,71 @@ __global__ __launch_bounds__(kRouteThreads) void route_offsets_kernel(
   }
 }
 
-// Workgroup e < num_experts places expert e's tokens; workgroup num_experts
-// marks the rows past the last run as padding.
+// Workgroup e < num_experts places expert e's tokens in ascending token
+// order: in each round of consecutive tokens an exclusive scan of the hits
+// gives each hit its rank.  Workgroup num_experts marks the rows past the
+// last run as padding.
 __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(
-    const int32_t* __restrict__ ids, int64_t tokens, int topk, int num_experts,
-    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ row_token, int64_t m_cap) {
-  const int e = blockIdx.x;
+    const int32_t* __restrict__ ids, int64_t tokens, int topk, int64_t tokens_per_split,
+    int num_experts, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ split_base, int32_t* __restrict__ row_token, int64_t m_cap) {
+  __shared__ int32_t chunk[kChunkLds];
+  const int e = blockIdx.x, sp = blockIdx.y;
   if (e == num_experts) {
-    for (int64_t r = offsets[num_experts] + threadIdx.x; r < m_cap; r += kRouteThreads)
-      row_token[r] = -1;
+    if (sp == 0)
+      for (int64_t r = offsets[num_experts] + threadIdx.x; r < m_cap; r += kRouteThreads)
+        row_token[r] = -1;
     return;
   }
-  const int64_t base = offsets[e];
-  int placed = 0;
-  for (int64_t t0 = 0; t0 < tokens; t0 += kRouteThreads) {
-    const int64_t t = t0 + threadIdx.x;
-    const int hit = t < tokens ? routes_to(ids, t, topk, e) : 0;
-    int total;
-    const int rank = block_exclusive_scan(hit, &total);
-    if (hit) row_token[base + placed + rank] = (int32_t)t;
-    placed += total;
+  const int64_t first = (int64_t)sp * tokens_per_split;
+  const int64_t last = first + tokens_per_split < tokens ? first + tokens_per_split : tokens;
+  const int64_t base = offsets[e] + split_base[(int64_t)e * gridDim.y + sp];
+  const IdChunks ch(ids, last, topk);
+  int32_t v[kIdsPerThread];
+  if (first < last) ch.load(first, v);
+  int64_t placed = 0;
+  for (int64_t t0 = first; t0 < last; t0 += ch.ct) {
+    __syncthreads();
+    ch.store(v, chunk);
+    __syncthreads();
+    if (t0 + ch.ct < last) ch.load(t0 + ch.ct, v);
+    const int64_t nt = ch.count(t0);
+    for (int r0 = 0; r0 < nt; r0 += kRouteThreads) {
+      const int t = r0 + threadIdx.x;
+      const int h = t < nt ? ch.hit(chunk, t, e) : 0;
+      int total;
+      const int rank = block_exclusive_scan(h, &total);
+      if (h) row_token[base + placed + rank] = (int32_t)(t0 + t);
+      placed += total;
+    }
   }
-  const int64_t end = offsets[e + 1];
-  for (int64_t r = base + counts[e] + threadIdx.x; r < end; r += kRouteThreads) row_token[r] = -1;
+  if (sp == 0) {   // the padding rows at the end of the expert's run
+    const int64_t end = offsets[e + 1];
+    for (int64_t r = offsets[e] + counts[e] + threadIdx.x; r < end; r += kRouteThreads)
+      row_token[r] = -1;
+  }
 }
 
 hipError_t launch_route_quantize(const void* x, bool bf16, int64_t tokens, int64_t hidden,
                                  const int32_t* ids, int topk, int num_experts, int64_t m_cap,
                                  uint8_t* q, float* sa, int32_t* block_expert, int32_t* row_token,
                                  int32_t* counts, int32_t* offsets, hipStream_t stream) {
-  hipLaunchKernelGGL(route_count_kernel, dim3(num_experts), dim3(kRouteThreads), 0, stream, ids,
-                     tokens, topk, counts);
-  hipLaunchKernelGGL(route_offsets_kernel, dim3(1), dim3(kRouteThreads), 0, stream, counts,
-                     num_experts, offsets, block_expert, m_cap / kGroup);
-  hipLaunchKernelGGL(route_place_kernel, dim3(num_experts + 1), dim3(kRouteThreads), 0, stream,
-                     ids, tokens, topk, num_experts, counts, offsets, row_token, m_cap);
+  // token ranges of about one chunk each, at most kMaxRouteSplits of them; the
+  // range counts live in the first num_experts * splits words of sa, which
+  // the gathered quantize overwrites afterwards (sa holds m_cap * hidden/128
+  // >= m_cap >= 127 * num_experts words)
+  const int64_t ct = kChunkInts / topk;
+  int64_t splits = (tokens + ct - 1) / ct;
+  if (splits > kMaxRouteSplits) splits = kMaxRouteSplits;
+  const int64_t per = (tokens + splits - 1) / splits;
+  int32_t* split_counts = reinterpret_cast<int32_t*>(sa);
+  hipLaunchKernelGGL(route_count_kernel, dim3(num_experts, (unsigned)splits), dim3(kRouteThreads),
+                     0, stream, ids, tokens, topk, per, split_counts);
+  hipLaunchKernelGGL(route_offsets_kernel, dim3(1), dim3(kRouteThreads), 0, stream, split_counts,
+                     (int)splits, counts, num_experts, offsets, block_expert, m_cap / kGroup);
+  hipLaunchKernelGGL(route_place_kernel, dim3(num_experts + 1, (unsigned)splits),
+                     dim3(kRouteThreads), 0, stream, ids, tokens, topk, per, num_experts, counts,
+                     offsets, split_counts, row_token, m_cap);
   if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   return launch_quantize_gather(x, bf16, row_token, m_cap, hidden, q, sa, stream);
 }

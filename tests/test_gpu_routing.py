@@ -103,6 +103,26 @@ def test_edge_routings(dev, name, bf16):
     _check_rows(got, wide, rt, np.arange(m_cap))
 
 
+def test_token_ranges_spanning_several_chunks(dev):
+    """A top-128 routing of 5000 tokens: the kernels cut the token axis into
+    their maximum number of ranges, each spanning more than one staged chunk
+    of ids, so the cross-range and cross-chunk rank bookkeeping is exercised.
+    The layout is checked whole, the quantized rows on a sample."""
+    T, H, k, E = 5000, 128, 128, 6
+    g = np.random.default_rng(407)
+    ids = g.integers(-1, E + 1, size=(T, k)).astype(np.int32)
+    ids[::3] = np.arange(k) % E                     # every third token hits every expert
+    x = g.standard_normal((T, H)).astype(np.float32)
+    m_cap = routing.capacity(T, k, E)
+    got, wide = _run(x, ids, E, m_cap, False)
+    rt = _check_layout(got, ids, E, m_cap)
+    off = got["expert_offsets"]
+    rows = np.unique(np.clip(np.concatenate([off[:-1], off[1:] - 1, off[:-1] + got["expert_counts"],
+                                             g.integers(0, int(off[-1]) + 256, 1500)]),
+                             0, m_cap - 1))
+    _check_rows(got, wide, rt, rows)
+
+
 @pytest.mark.parametrize("bf16", [False, True])
 def test_full_size_zipf(dev, bf16):
     """8192 tokens x 7168 hidden, top-8 of 32 experts with Zipf(1.1)
