@@ -7,13 +7,15 @@
 // blocks), plus MX blocks of 32 elements sharing one power-of-two exponent
 // (aitrends.kr B200 article, MXFP8 glossary entry).
 //
-// All three kernels are HBM-bound streams (4 B read + ~1.03 B written per
-// element): float4 loads, amax by butterfly exchanges inside the lanes that
-// hold one group, one packed 4-byte store of codes per lane.  Results are
-// bit-exact with the format rules in fg8.h: the scale is the correctly
-// rounded float32 quotient amax / 448, elements use a correctly rounded
-// float32 division by it, and the MX exponent comes straight from the float
-// bits of amax.
+// The kernels are HBM-bound streams (4 or 2 B read + ~1.03 B written per
+// element): wide loads, the amax of a group by butterfly exchanges among the
+// lanes that hold it (or through LDS where a group spans waves), packed
+// stores of codes.  A fourth kind groups 128 rows of each column instead of
+// 128 columns of each row and writes the codes transposed (the token-axis
+// quantization of the weight gradient).  Results are bit-exact with the
+// format rules in fg8.h: the scale is the correctly rounded float32 quotient
+// amax / 448, elements use a correctly rounded float32 division by it, and
+// the MX exponent comes straight from the float bits of amax.
 #include "fg8_device.h"
 #include "fg8_internal.h"
 
