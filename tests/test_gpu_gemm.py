@@ -57,6 +57,8 @@ CASES = [
     ("tiny", 17, 130, 256),
     ("prefill_b", 65, 2112, 7168),               # just past the skinny path
     ("skinny_a", 7, 8192, 4096),
+    ("tiny", 64, 64, 16384),                     # largest K: 128 K blocks, 8-way split-K
+    ("prefill_a", 100, 392, 512),                # 64 < M <= 128 path, ragged M and N
 ]
 
 

@@ -280,6 +280,27 @@ def test_masked_counts_are_clamped(dev):
                       S_flush=F)
 
 
+def test_masked_all_counts_zero_writes_nothing(dev):
+    """Every expert empty: no tile is enumerated and the output keeps its
+    sentinel everywhere (the FP8 and the MXFP8 masked paths)."""
+    E, cap, N, K = 4, 128, 256, 512
+    v = np.zeros(E, np.int32)
+    _, a, b = _masked_inputs(E, cap, N, K, valid=np.full(E, cap, np.int32))
+    qa, sa = scaling.quantize_1x128(a)
+    qb, sb = scaling.quantize_128x128(b)
+    ta, tsa, tb, tsb, tv = _gpu(qa, sa, qb, sb, v)
+    out = torch.full((E, cap, N), float(SENTINEL_F32), dtype=torch.float32, device="cuda")
+    fg8.grouped_gemm_fp8_masked(ta, tsa, tb, tsb, tv, out=out)
+    qx, ex = scaling.quantize_mx(a)
+    qy, ey = scaling.quantize_mx(b)
+    out_mx = torch.full((E, cap, N), float(SENTINEL_F32), dtype=torch.float32, device="cuda")
+    tx, tex, ty, tey = _gpu(qx, ex, qy, ey)
+    fg8.gemm_mxfp8(tx, tex, ty, tey, tv, out=out_mx)
+    torch.cuda.synchronize()
+    assert np.all(out.cpu().numpy() == SENTINEL_F32)
+    assert np.all(out_mx.cpu().numpy() == SENTINEL_F32)
+
+
 def test_masked_full_size_sampled(dev):
     """16 experts x 256 rows, N=4096, K=7168, counts ~ U{0..256}: all columns
     computed on the GPU, two 128-column blocks of every expert checked."""
