@@ -85,8 +85,9 @@ def rotations(nbytes):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported in this build "
-              "(the multi-GPU layout is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the kernels "
+              "run on one GPU's share of the work, and sharding N (dense) or the experts "
+              "(grouped) across GPUs is not part of this library", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
