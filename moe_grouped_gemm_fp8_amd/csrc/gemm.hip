@@ -12,7 +12,7 @@
 // section) instead hands each lane's E8M0 byte to
 // v_mfma_scale_f32_16x16x128_f8f6f4 and accumulates straight through K.
 //
-// Work decomposition (one wavefront = 64 lanes, 4 waves per workgroup):
+// Work decomposition (one wavefront = 64 lanes, 4 or 8 waves per workgroup):
 //   * a workgroup owns a BM x BN output tile; waves split it WAVES_M x WAVES_N;
 //     each wave holds its (BM/WAVES_M) x (BN/WAVES_N) FP32 accumulators in
 //     VGPRs as 16x16 MFMA tiles;
@@ -25,8 +25,11 @@
 //     from 16 consecutive rows) hit distinct banks;
 //   * a persistent grid walks a linear list of work units: dense tiles
 //     (optionally split along K with a deterministic last-arriver reduction),
-//     contiguous-layout tiles whose expert comes from block_expert, or
-//     masked-layout tiles enumerated from the device-side valid counts.
+//     contiguous-layout tiles whose expert comes from block_expert (with an
+//     optional gated epilogue that quantizes the activation for the next
+//     GEMM), masked-layout tiles enumerated from the device-side valid
+//     counts, or K-grouped tiles whose K range comes from per-group offsets
+//     (the weight gradient, 1x128 scales on both operands).
 //
 // Lane layout (measured on gfx950 by the probe tests): in the 16x16x128 MFMA
 // lane l = i + 16 g holds row i of A (column i of B) with K = 16 g .. 16 g + 15
