@@ -52,6 +52,26 @@ def contiguous_layout(topk_ids, num_experts: int, m_cap: int):
     return row_token, block_expert, offsets, counts
 
 
+def token_rows(topk_ids, num_experts: int, m_cap: int):
+    """The inverse of the layout's row map: int32 [T, k] whose entry (t, j) is
+    the row holding token t's copy for its j-th expert id, or -1 where that id
+    routes nowhere (outside [0, E)) or repeats an earlier id of the same
+    token (the token has one row per distinct expert).  This is the map the
+    step after the second expert GEMM needs to bring each token's k rows
+    back; it is read off the layout defined above."""
+    ids = np.asarray(topk_ids)
+    row_token, block_expert, _, _ = contiguous_layout(ids, num_experts, m_cap)
+    out = np.full(ids.shape, -1, np.int32)
+    for r in range(m_cap):
+        t = int(row_token[r])
+        if t < 0:
+            continue
+        e = int(block_expert[r // GROUP])
+        j = int(np.nonzero(ids[t] == e)[0][0])     # the first position holding e
+        out[t, j] = r
+    return out
+
+
 def gather_quantize(x, row_token):
     """Rows x[row_token[r]] (zeros where row_token[r] < 0) quantized 1x128:
     (q uint8 [m_cap, H], s float32 [H/128, m_cap])."""

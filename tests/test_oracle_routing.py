@@ -57,3 +57,36 @@ def test_gather_quantize_is_the_quantizer_on_gathered_rows():
             assert np.array_equal(q[r], qr[0]) and np.array_equal(s[:, r], sr[:, 0])
     pad = rt < 0
     assert np.all(q[pad] == 0) and np.all(s[:, pad] == 1.0)
+
+
+def test_token_rows_hand_worked():
+    """The inverse map of the hand-worked routing: expert 0 holds tokens
+    0, 1, 2, 4 in rows 0..3, expert 2 holds tokens 0, 1, 3 in rows 128..130;
+    repeated ids and the out-of-range id 9 get -1."""
+    ids = np.array([[0, 2], [2, 0], [0, 0], [2, 2], [9, 0]])
+    tr = routing.token_rows(ids, 3, 512)
+    assert tr.tolist() == [[0, 128], [129, 1], [2, -1], [130, -1], [-1, 3]]
+
+
+def test_token_rows_invert_the_row_map():
+    g = np.random.default_rng(12)
+    for T, k, E in [(200, 4, 7), (97, 8, 3), (300, 2, 64)]:
+        ids = g.integers(-1, E + 1, size=(T, k))
+        m_cap = routing.capacity(T, k, E)
+        rt, be, off, cnt = routing.contiguous_layout(ids, E, m_cap)
+        tr = routing.token_rows(ids, E, m_cap)
+        live = tr >= 0
+        # every row that holds a token is named exactly once, by that token,
+        # at a position whose id is the row's expert
+        assert np.array_equal(np.sort(tr[live]), np.sort(np.nonzero(rt >= 0)[0]))
+        t_idx, j_idx = np.nonzero(live)
+        assert np.array_equal(rt[tr[live]], t_idx)
+        assert np.array_equal(be[tr[live] // 128], ids[t_idx, j_idx])
+        # -1 exactly where the id is out of range or repeats an earlier one
+        for t in range(T):
+            seen = set()
+            for j in range(k):
+                e = int(ids[t, j])
+                dead = not (0 <= e < E) or e in seen
+                seen.add(e)
+                assert (tr[t, j] == -1) == dead
