@@ -406,11 +406,10 @@ def run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launch
                steps=20)
         del qa, ea, qw, ew, d1
 
-    # MoE routing -> contiguous layout + 1x128 quantize of the gathered BF16
-    # token rows (the step before the contiguous W1 GEMM).  Bytes: the token
-    # rows read once, the ids, and the layout's codes, scales and index arrays
-    # written; each routed row is gathered once per expert that picked it, the
-    # repeats served by the caches when they hit.
+    # MoE routing -> contiguous layout + 1x128 quantize of the BF16 token rows
+    # into the rows that hold them (the step before the contiguous W1 GEMM).
+    # Bytes: every token row read once, the ids, and the layout's codes,
+    # scales, row map and its inverse written once.
     if want("route"):
         cc = inputs.ContiguousCase()
         ids = torch.from_numpy(inputs.zipf_topk_routing(cc.workload, cc.tokens, cc.experts,
@@ -419,14 +418,11 @@ def run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launch
         cap = fg8.moe_capacity(cc.tokens, cc.topk, cc.experts)
         lay = fg8.moe_contiguous_layout_fp8(x, ids, cc.experts)
         valid = int(lay["expert_counts"].sum())
-        nb = (2 * x.numel() + 4 * ids.numel() + cap * cc.hidden + 4 * cap * cc.hidden // 128
+        nb = (2 * x.numel() + 8 * ids.numel() + cap * cc.hidden + 4 * cap * cc.hidden // 128
               + 4 * cap + 4 * cap // 128 + 8 * cc.experts + 4)
-        record(f"moe routing + gather + quantize 1x128 from bf16 {cc.tokens}x{cc.hidden} "
+        record(f"moe routing + quantize 1x128 from bf16 into the layout {cc.tokens}x{cc.hidden} "
                f"top{cc.topk} of {cc.experts} (m_cap {cap}, routed {valid})",
                [lambda: fg8.moe_contiguous_layout_fp8(x, ids, cc.experts, out=lay)], nbytes=nb)
-        out[next(reversed(out))]["gbs_gathered"] = round(
-            (2 * valid * cc.hidden + nb - 2 * x.numel()) / (out[next(reversed(out))]["ms_graph"] * 1e-3)
-            / 1e9, 1)
         del x, ids, lay
 
     # Training backward of W1: dY and X quantized along the token axis

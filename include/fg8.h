@@ -281,12 +281,18 @@ fg8_status grouped_gemm_fp8_kgrouped(const uint8_t* a, const float* sa, const ui
  *   block_expert   int32 [m_cap/128]: expert of each 128-row block, -1 for
  *              the blocks past the last run (the contiguous GEMM skips them)
  *   row_token  int32 [m_cap]: source token of each row, -1 for padding
+ *   token_row  int32 [tokens][topk]: the inverse map, the row holding token
+ *              t's copy for its j-th id, -1 where that id routes nowhere or
+ *              repeats an earlier id of the token (what the step after the
+ *              second expert GEMM needs to bring a token's rows back)
  *   expert_offsets int32 [num_experts + 1]: first row of each expert's run;
  *              expert_offsets[num_experts] = rows in use
  *   expert_counts  int32 [num_experts]: tokens routed to each expert
  * Experts are laid out in id order, an expert's tokens in ascending token
- * order.  Padding rows quantize as zeros (code 0, scale 1), so every output
- * is written and the result is the same on every call.
+ * order.  Each token row is read and quantized once and written into every
+ * row that holds it; padding rows quantize as zeros (code 0, scale 1), so
+ * every output is written and the result is the same on every call.  sa
+ * doubles as scratch for the per-range counts before the scales are written.
  *   hidden % 128 == 0 (else FG8_EUNSUPPORTED); tokens >= 1;
  *   1 <= topk <= 256; 1 <= num_experts <= 1024; m_cap % 128 == 0 and
  *   m_cap >= fg8_moe_capacity(tokens, topk, num_experts), which holds any
@@ -296,8 +302,8 @@ fg8_status moe_contiguous_layout_fp8(const void* x, int32_t x_is_bf16, int64_t t
                                      int64_t hidden, const int32_t* topk_ids, int32_t topk,
                                      int32_t num_experts, int64_t m_cap, uint8_t* q, float* sa,
                                      int32_t* block_expert, int32_t* row_token,
-                                     int32_t* expert_offsets, int32_t* expert_counts,
-                                     hipStream_t stream);
+                                     int32_t* token_row, int32_t* expert_offsets,
+                                     int32_t* expert_counts, hipStream_t stream);
 
 /* Rows that hold any routing of `tokens` tokens with `topk` ids each over
  * `num_experts` experts: every routed row plus up to 127 padding rows per

@@ -41,7 +41,7 @@ _SIGNATURES = {
     "grouped_gemm_mxfp8_contiguous": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int,
                                       _c_i64, _c_i64, _c_i64, _c_i32, _c_ptr],
     "moe_contiguous_layout_fp8": [_c_ptr, _c_i32, _c_i64, _c_i64, _c_ptr, _c_i32, _c_i32, _c_i64,
-                                  _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr],
+                                  _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr],
     "fg8_moe_capacity": [_c_i64, _c_i32, _c_i32],
     "fg8_gemm_workspace_bytes": [_c_i64, _c_i64, _c_i64],
     "fg8_last_error": [],
@@ -331,9 +331,10 @@ def moe_capacity(tokens, topk, num_experts) -> int:
 def moe_contiguous_layout_fp8(x, topk_ids, num_experts, m_cap=None, out=None):
     """x float32 or bfloat16 [tokens, hidden], topk_ids int32 [tokens, topk]
     (device) -> dict of q uint8 [m_cap, hidden], sa [hidden/128, m_cap],
-    block_expert int32 [m_cap/128], row_token int32 [m_cap],
-    expert_offsets int32 [E + 1], expert_counts int32 [E], all on the device:
-    the operands of grouped_gemm_fp8_contiguous plus the row map.  `out`, a
+    block_expert int32 [m_cap/128], row_token int32 [m_cap], token_row int32
+    [tokens, topk], expert_offsets int32 [E + 1], expert_counts int32 [E], all
+    on the device: the operands of grouped_gemm_fp8_contiguous plus the row
+    map and its inverse.  `out`, a
     dict like the one returned, gives the buffers to fill."""
     bf16 = x.dtype == torch.bfloat16
     _dev(x, torch.bfloat16 if bf16 else torch.float32, "x")
@@ -347,6 +348,7 @@ def moe_contiguous_layout_fp8(x, topk_ids, num_experts, m_cap=None, out=None):
     dev = x.device
     shapes = {"q": ((m_cap, hidden), torch.uint8), "sa": ((hidden // 128, m_cap), torch.float32),
               "block_expert": ((m_cap // 128,), torch.int32), "row_token": ((m_cap,), torch.int32),
+              "token_row": ((tokens, topk), torch.int32),
               "expert_offsets": ((num_experts + 1,), torch.int32),
               "expert_counts": ((num_experts,), torch.int32)}
     if out is not None:
@@ -360,5 +362,6 @@ def moe_contiguous_layout_fp8(x, topk_ids, num_experts, m_cap=None, out=None):
     _check(lib().moe_contiguous_layout_fp8(
         _ptr(x), int(bf16), tokens, hidden, _ptr(topk_ids), topk, num_experts, m_cap,
         _ptr(out["q"]), _ptr(out["sa"]), _ptr(out["block_expert"]), _ptr(out["row_token"]),
-        _ptr(out["expert_offsets"]), _ptr(out["expert_counts"]), _stream()))
+        _ptr(out["token_row"]), _ptr(out["expert_offsets"]), _ptr(out["expert_counts"]),
+        _stream()))
     return out

@@ -340,8 +340,8 @@ fg8_status moe_contiguous_layout_fp8(const void* x, int32_t x_is_bf16, int64_t t
                                      int64_t hidden, const int32_t* topk_ids, int32_t topk,
                                      int32_t num_experts, int64_t m_cap, uint8_t* q, float* sa,
                                      int32_t* block_expert, int32_t* row_token,
-                                     int32_t* expert_offsets, int32_t* expert_counts,
-                                     hipStream_t stream) {
+                                     int32_t* token_row, int32_t* expert_offsets,
+                                     int32_t* expert_counts, hipStream_t stream) {
   const char* fn = "moe_contiguous_layout_fp8";
   FG8_CHECK_PTR(x);
   FG8_CHECK_PTR(topk_ids);
@@ -349,6 +349,7 @@ fg8_status moe_contiguous_layout_fp8(const void* x, int32_t x_is_bf16, int64_t t
   FG8_CHECK_PTR(sa);
   FG8_CHECK_PTR(block_expert);
   FG8_CHECK_PTR(row_token);
+  FG8_CHECK_PTR(token_row);
   FG8_CHECK_PTR(expert_offsets);
   FG8_CHECK_PTR(expert_counts);
   if (x_is_bf16 != 0 && x_is_bf16 != 1)
@@ -368,7 +369,8 @@ fg8_status moe_contiguous_layout_fp8(const void* x, int32_t x_is_bf16, int64_t t
                 (long long)m_cap, (long long)need);
   const hipError_t e = fg8::launch_route_quantize(x, x_is_bf16 == 1, tokens, hidden, topk_ids, topk,
                                                   num_experts, m_cap, q, sa, block_expert,
-                                                  row_token, expert_counts, expert_offsets, stream);
+                                                  row_token, token_row, expert_counts,
+                                                  expert_offsets, stream);
   if (e != hipSuccess) return fail(FG8_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   g_err[0] = 0;
   return FG8_OK;

@@ -49,4 +49,29 @@ __device__ __forceinline__ float abs_max4(float4 v) {
   return fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
 }
 
+// Sixteen bytes of a row as FP32: four floats, or eight BF16 values (raw
+// 16-bit words) widened exactly.
+template <class T>
+struct RowVec;
+template <>
+struct RowVec<float> {
+  static constexpr int kElems = 4;
+  __device__ static void widen(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+  }
+};
+template <>
+struct RowVec<uint16_t> {   // BF16 bits widen exactly to FP32
+  static constexpr int kElems = 8;
+  __device__ static void widen(const uint4& u, float* f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
 }  // namespace fg8

@@ -64,16 +64,14 @@ hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t stream);
 
 hipError_t launch_quantize(const void* x, bool bf16, int64_t batch, int64_t rows, int64_t cols,
                            int kind, uint8_t* q, void* scales, hipStream_t stream);
-// 1x128 quantize of rows gathered by index: output row r takes source row
-// row_src[r], or zeros where row_src[r] < 0.
-hipError_t launch_quantize_gather(const void* x, bool bf16, const int32_t* row_src, int64_t rows,
-                                  int64_t cols, uint8_t* q, float* scales, hipStream_t stream);
 // Top-k routing ids -> contiguous layout (counts, offsets, block_expert,
-// row_token) followed by the gathered 1x128 quantize.
+// row_token, token_row) followed by the 1x128 quantize of every token row
+// into the rows it owns.
 hipError_t launch_route_quantize(const void* x, bool bf16, int64_t tokens, int64_t hidden,
                                  const int32_t* ids, int topk, int num_experts, int64_t m_cap,
                                  uint8_t* q, float* sa, int32_t* block_expert, int32_t* row_token,
-                                 int32_t* counts, int32_t* offsets, hipStream_t stream);
+                                 int32_t* token_row, int32_t* counts, int32_t* offsets,
+                                 hipStream_t stream);
 
 int device_cu_count();
 

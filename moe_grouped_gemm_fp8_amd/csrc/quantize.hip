@@ -43,36 +43,11 @@ __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* p) {
 // 16-byte loads, kQUnroll of them in flight per lane.  One load instruction of
 // a wave covers 64 x 16 bytes = 2 (FP32) or 4 (BF16) groups of 128 columns; the
 // 32 or 16 lanes that hold a group reduce its amax with butterfly exchanges.
-// Scales are written K-block major.  With GATHER, output row r quantizes source
-// row row_src[r] (a row of zeros where that is negative).
+// Scales are written K-block major.
 constexpr int kQUnroll = 8;
 
 template <class T>
-struct RowVec;
-template <>
-struct RowVec<float> {
-  static constexpr int kElems = 4;
-  __device__ static void widen(const uint4& u, float* f) {
-    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
-    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
-  }
-};
-template <>
-struct RowVec<uint16_t> {   // BF16 bits widen exactly to FP32
-  static constexpr int kElems = 8;
-  __device__ static void widen(const uint4& u, float* f) {
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-  }
-};
-
-template <class T, bool GATHER>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const T* __restrict__ x,
-                                                          const int32_t* __restrict__ row_src,
                                                           uint8_t* __restrict__ q,
                                                           float* __restrict__ s, int64_t rows,
                                                           int64_t cols, int64_t seg_cols,
@@ -89,9 +64,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const T* __restrict__ 
     const int64_t c_begin = (it - grow * nseg) * seg_cols;
     const int64_t c_end = c_begin + seg_cols < cols ? c_begin + seg_cols : cols;
     const int64_t b = grow / rows, r = grow - b * rows;
-    int64_t src = grow;
-    if constexpr (GATHER) src = row_src[grow];
-    const T* xr = x + (src >= 0 ? src : 0) * cols;
+    const T* xr = x + grow * cols;
     uint8_t* qr = q + grow * cols;
     float* sb = s + b * (cols / kGroup) * rows + r;
     for (int64_t c0 = c_begin; c0 < c_end; c0 += kQUnroll * SPAN) {
@@ -99,8 +72,7 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const T* __restrict__ 
 #pragma unroll
       for (int u = 0; u < kQUnroll; ++u) {
         const int64_t col = c0 + u * SPAN + lane * EPL;
-        raw[u] = src >= 0 && col < c_end ? *reinterpret_cast<const uint4*>(xr + col)
-                                         : make_uint4(0, 0, 0, 0);
+        raw[u] = col < c_end ? *reinterpret_cast<const uint4*>(xr + col) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < kQUnroll; ++u) {
@@ -140,15 +112,15 @@ static int64_t q1_seg_cols(int64_t rows, int64_t cols, int elems) {
   return per * span;
 }
 
-template <class T, bool GATHER>
-static hipError_t launch_q1(const T* x, const int32_t* row_src, int64_t rows_all, int64_t rows,
-                            int64_t cols, uint8_t* q, float* s, hipStream_t stream) {
+template <class T>
+static hipError_t launch_q1(const T* x, int64_t rows_all, int64_t rows, int64_t cols, uint8_t* q,
+                            float* s, hipStream_t stream) {
   const int64_t seg = q1_seg_cols(rows_all, cols, RowVec<T>::kElems);
   const int64_t items = rows_all * ((cols + seg - 1) / seg);
   const int64_t blocks = (items + 3) / 4;
   const unsigned grid = (unsigned)(blocks < (1 << 20) ? blocks : (1 << 20));
-  hipLaunchKernelGGL((quant_1x128_kernel<T, GATHER>), dim3(grid), dim3(256), 0, stream, x, row_src,
-                     q, s, rows, cols, seg, items);
+  hipLaunchKernelGGL(quant_1x128_kernel<T>, dim3(grid), dim3(256), 0, stream, x, q, s, rows, cols,
+                     seg, items);
   return hipGetLastError();
 }
 
@@ -288,7 +260,7 @@ template <class T>
 static hipError_t launch_quantize_t(const T* x, int64_t batch, int64_t rows, int64_t cols, int kind,
                                     uint8_t* q, void* scales, hipStream_t stream) {
   if (kind == 0) {
-    return launch_q1<T, false>(x, nullptr, batch * rows, rows, cols, q, (float*)scales, stream);
+    return launch_q1<T>(x, batch * rows, rows, cols, q, (float*)scales, stream);
   } else if (kind == 1) {
     dim3 grid((unsigned)(cols / kGroup), (unsigned)((rows + kGroup - 1) / kGroup), (unsigned)batch);
     hipLaunchKernelGGL(quant_128x128_kernel<T>, grid, dim3(256), 0, stream, x, q, (float*)scales,
@@ -312,14 +284,6 @@ hipError_t launch_quantize(const void* x, bool bf16, int64_t batch, int64_t rows
   if (bf16)
     return launch_quantize_t((const uint16_t*)x, batch, rows, cols, kind, q, scales, stream);
   return launch_quantize_t((const float*)x, batch, rows, cols, kind, q, scales, stream);
-}
-
-hipError_t launch_quantize_gather(const void* x, bool bf16, const int32_t* row_src, int64_t rows,
-                                  int64_t cols, uint8_t* q, float* scales, hipStream_t stream) {
-  if (bf16)
-    return launch_q1<uint16_t, true>((const uint16_t*)x, row_src, rows, rows, cols, q, scales,
-                                     stream);
-  return launch_q1<float, true>((const float*)x, row_src, rows, rows, cols, q, scales, stream);
 }
 
 }  // namespace fg8

@@ -1,5 +1,5 @@
 // MoE routing -> contiguous grouped-GEMM layout, with the 1x128 quantization
-// of the gathered rows fused in.
+// of the token rows fused in.
 //
 // The contiguous layout of DeepGEMM's MoE grouped GEMM (release news,
 // ctol-kr.com, section 4) stacks the rows routed to each expert, expert after
@@ -14,10 +14,12 @@
 //   3. place: one workgroup per (expert, token range) walks its tokens in
 //      ascending order (a block-wide scan gives each token its rank) and
 //      writes row_token;
-//   4. gather + quantize: 1x128 groups of the source row of every layout row
-//      (zeros, scale 1, for padding), as the 1x128 quantizer does.
+//   4. quantize + scatter: each token row is read once, quantized 1x128 as
+//      the 1x128 quantizer does, and its codes and scales are written into
+//      every row that holds the token (token_row, the inverse of row_token,
+//      written by steps 1 and 3); padding rows get code 0, scale 1.
 // Steps 1-3 read only the ids (tokens x top-k int32); step 4 is the HBM
-// stream: one read of every routed row, one write of the FP8 codes.
+// stream: one read of every token row, one write of every layout row.
 #include "fg8_device.h"
 #include "fg8_internal.h"
 
@@ -69,6 +71,21 @@ struct IdChunks {
     for (int j = 0; j < topk; ++j) h |= lds[j * stride + t] == e;
     return h;
   }
+  // The first position of expert e in chunk token t's ids.
+  __device__ int first(const int32_t* lds, int t, int e) const {
+    int j = 0;
+    while (lds[j * stride + t] != e) ++j;   // only called for a hit
+    return j;
+  }
+  // Does position j of chunk token t route nowhere (an id outside [0, E) or
+  // a repeat of an earlier id of the token)?
+  __device__ bool dead(const int32_t* lds, int t, int j, int num_experts) const {
+    const int id = lds[j * stride + t];
+    if (id < 0 || id >= num_experts) return true;
+    for (int i = 0; i < j; ++i)
+      if (lds[i * stride + t] == id) return true;
+    return false;
+  }
 };
 
 // Block-wide exclusive scan of one int per thread; also returns the total.
@@ -98,9 +115,11 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total) {
 // The token axis is cut into `splits` ranges of tokens_per_split tokens;
 // workgroup (e, s) examines range s for expert e, so that every range is about
 // one chunk.  The per-range counts go to split_counts[e * splits + s].
+// The expert-0 workgroup of each range also marks the top-k positions that
+// route nowhere (token_row = -1); the place kernel fills in the others.
 __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(
     const int32_t* __restrict__ ids, int64_t tokens, int topk, int64_t tokens_per_split,
-    int32_t* __restrict__ split_counts) {
+    int num_experts, int32_t* __restrict__ split_counts, int32_t* __restrict__ token_row) {
   __shared__ int32_t chunk[kChunkLds];
   const int e = blockIdx.x, sp = blockIdx.y;
   const int64_t first = (int64_t)sp * tokens_per_split;
@@ -115,7 +134,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_count_kernel(
     __syncthreads();
     if (t0 + ch.ct < last) ch.load(t0 + ch.ct, v);   // in flight meanwhile
     const int64_t nt = ch.count(t0);
-    for (int t = threadIdx.x; t < nt; t += kRouteThreads) n += ch.hit(chunk, t, e);
+    for (int t = threadIdx.x; t < nt; t += kRouteThreads) {
+      n += ch.hit(chunk, t, e);
+      if (e == 0)
+        for (int j = 0; j < topk; ++j)
+          if (ch.dead(chunk, t, j, num_experts)) token_row[(t0 + t) * topk + j] = -1;
+    }
   }
   int total;
   block_exclusive_scan(n, &total);
@@ -171,7 +195,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_offsets_kernel(
 __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(
     const int32_t* __restrict__ ids, int64_t tokens, int topk, int64_t tokens_per_split,
     int num_experts, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ split_base, int32_t* __restrict__ row_token, int64_t m_cap) {
+    const int32_t* __restrict__ split_base, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ token_row, int64_t m_cap) {
   __shared__ int32_t chunk[kChunkLds];
   const int e = blockIdx.x, sp = blockIdx.y;
   if (e == num_experts) {
@@ -198,7 +223,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(
       const int h = t < nt ? ch.hit(chunk, t, e) : 0;
       int total;
       const int rank = block_exclusive_scan(h, &total);
-      if (h) row_token[base + placed + rank] = (int32_t)(t0 + t);
+      if (h) {
+        const int64_t row = base + placed + rank;
+        row_token[row] = (int32_t)(t0 + t);
+        token_row[(t0 + t) * topk + ch.first(chunk, t, e)] = (int32_t)row;
+      }
       placed += total;
     }
   }
@@ -209,28 +238,113 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(
   }
 }
 
+// 1x128 quantize of every token row, written into each row of the layout
+// that holds the token (token_row), plus the padding rows (zeros: code 0,
+// scale 1).  Items [0, tokens) are token rows, one wave each, read once and
+// quantized once with 16-byte loads; items tokens + b clear the padding rows
+// of 128-row block b.
+template <class T>
+__global__ __launch_bounds__(256) void route_scatter_quant_kernel(
+    const T* __restrict__ x, const int32_t* __restrict__ token_row,
+    const int32_t* __restrict__ row_token, uint8_t* __restrict__ q, float* __restrict__ sa,
+    int64_t tokens, int topk, int64_t hidden, int64_t m_cap) {
+  constexpr int EPL = RowVec<T>::kElems;   // elements per lane per load
+  constexpr int LPG = kGroup / EPL;        // lanes per 128-column group
+  constexpr int SPAN = 64 * EPL;           // columns per wave load
+  constexpr int U = 4;                     // loads in flight per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t items = tokens + m_cap / kGroup;
+  for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < items;
+       it += (int64_t)gridDim.x * 4) {
+    if (it < tokens) {
+      const T* xr = x + it * hidden;
+      const int32_t* rows = token_row + it * topk;
+      for (int64_t c0 = 0; c0 < hidden; c0 += U * SPAN) {
+        uint4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t col = c0 + u * SPAN + lane * EPL;
+          raw[u] = col < hidden ? *reinterpret_cast<const uint4*>(xr + col) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t col = c0 + u * SPAN + lane * EPL;
+          float f[EPL];
+          RowVec<T>::widen(raw[u], f);
+          float m = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) m = fmaxf(m, fabsf(f[e]));
+          const float amax = group_max<LPG>(m);
+          const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
+          uint32_t code[EPL / 4];
+#pragma unroll
+          for (int e = 0; e < EPL / 4; ++e)
+            code[e] = pack4_e4m3(make_float4(f[4 * e] / sc, f[4 * e + 1] / sc, f[4 * e + 2] / sc,
+                                             f[4 * e + 3] / sc));
+          if (col < hidden) {
+            for (int j = 0; j < topk; ++j) {
+              const int64_t r = rows[j];
+              if (r < 0) continue;
+              if constexpr (EPL == 4)
+                *reinterpret_cast<uint32_t*>(q + r * hidden + col) = code[0];
+              else
+                *reinterpret_cast<uint2*>(q + r * hidden + col) = make_uint2(code[0], code[1]);
+              if ((lane & (LPG - 1)) == 0) sa[(col / kGroup) * m_cap + r] = sc;
+            }
+          }
+        }
+      }
+    } else {
+      // padding rows of one 128-row block: code 0, scale 1
+      const int64_t r0 = (it - tokens) * kGroup;
+      for (int h = 0; h < 2; ++h) {
+        const int64_t mine = r0 + h * 64 + lane;
+        uint64_t pad = __ballot(row_token[mine] < 0);
+        while (pad) {
+          const int i = __builtin_ctzll(pad);
+          pad &= pad - 1;
+          const int64_t r = r0 + h * 64 + i;
+          for (int64_t c = (int64_t)lane * 16; c < hidden; c += 64 * 16)
+            *reinterpret_cast<uint4*>(q + r * hidden + c) = make_uint4(0, 0, 0, 0);
+          for (int64_t kb = lane; kb < hidden / kGroup; kb += 64) sa[kb * m_cap + r] = 1.f;
+        }
+      }
+    }
+  }
+}
+
 hipError_t launch_route_quantize(const void* x, bool bf16, int64_t tokens, int64_t hidden,
                                  const int32_t* ids, int topk, int num_experts, int64_t m_cap,
                                  uint8_t* q, float* sa, int32_t* block_expert, int32_t* row_token,
-                                 int32_t* counts, int32_t* offsets, hipStream_t stream) {
+                                 int32_t* token_row, int32_t* counts, int32_t* offsets,
+                                 hipStream_t stream) {
   // token ranges of about one chunk each, at most kMaxRouteSplits of them; the
-  // range counts live in the first num_experts * splits words of sa, which
-  // the gathered quantize overwrites afterwards (sa holds m_cap * hidden/128
-  // >= m_cap >= 127 * num_experts words)
+  // range counts live in the first num_experts * splits words of sa until the
+  // place kernel has read them (sa holds m_cap * hidden/128 >= m_cap >= 127 *
+  // num_experts words); the quantize that overwrites sa runs after it
   const int64_t ct = kChunkInts / topk;
   int64_t splits = (tokens + ct - 1) / ct;
   if (splits > kMaxRouteSplits) splits = kMaxRouteSplits;
   const int64_t per = (tokens + splits - 1) / splits;
   int32_t* split_counts = reinterpret_cast<int32_t*>(sa);
   hipLaunchKernelGGL(route_count_kernel, dim3(num_experts, (unsigned)splits), dim3(kRouteThreads),
-                     0, stream, ids, tokens, topk, per, split_counts);
+                     0, stream, ids, tokens, topk, per, num_experts, split_counts, token_row);
   hipLaunchKernelGGL(route_offsets_kernel, dim3(1), dim3(kRouteThreads), 0, stream, split_counts,
                      (int)splits, counts, num_experts, offsets, block_expert, m_cap / kGroup);
   hipLaunchKernelGGL(route_place_kernel, dim3(num_experts + 1, (unsigned)splits),
                      dim3(kRouteThreads), 0, stream, ids, tokens, topk, per, num_experts, counts,
-                     offsets, split_counts, row_token, m_cap);
-  if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  return launch_quantize_gather(x, bf16, row_token, m_cap, hidden, q, sa, stream);
+                     offsets, split_counts, row_token, token_row, m_cap);
+  const int64_t items = tokens + m_cap / kGroup;
+  const int64_t blocks = (items + 3) / 4;
+  const unsigned grid = (unsigned)(blocks < (1 << 20) ? blocks : (1 << 20));
+  if (bf16)
+    hipLaunchKernelGGL(route_scatter_quant_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
+                       (const uint16_t*)x, token_row, row_token, q, sa, tokens, topk, hidden,
+                       m_cap);
+  else
+    hipLaunchKernelGGL(route_scatter_quant_kernel<float>, dim3(grid), dim3(256), 0, stream,
+                       (const float*)x, token_row, row_token, q, sa, tokens, topk, hidden, m_cap);
+  return hipGetLastError();
 }
 
 }  // namespace fg8

@@ -132,12 +132,12 @@ def test_moe_layout_validation(L):
     ok = _fake(0x10000)
     f = L.moe_contiguous_layout_fp8
     f.argtypes = [P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, P, ctypes.c_int32,
-                  ctypes.c_int32, ctypes.c_int64, P, P, P, P, P, P, P]
+                  ctypes.c_int32, ctypes.c_int64, P, P, P, P, P, P, P, P]
 
     def call(x=ok, bf16=0, tokens=8192, hidden=7168, ids=ok, topk=8, experts=32, m_cap=69632,
              offsets=ok):
-        return f(x, bf16, tokens, hidden, ids, topk, experts, m_cap, ok, ok, ok, ok, offsets, ok,
-                 None)
+        return f(x, bf16, tokens, hidden, ids, topk, experts, m_cap, ok, ok, ok, ok, ok, offsets,
+                 ok, None)
 
     assert call(ids=None) == 1 and b"topk_ids is NULL" in L.fg8_last_error()
     assert call(offsets=_fake(0x10004)) == 1 and b"16-byte" in L.fg8_last_error()

@@ -41,6 +41,7 @@ def _run(x, ids, experts, m_cap=None, bf16=False):
 
 def _check_layout(got, ids, experts, m_cap):
     rt, be, off, cnt = routing.contiguous_layout(ids, experts, m_cap)
+    assert np.array_equal(got["token_row"], routing.token_rows(ids, experts, m_cap))
     assert np.array_equal(got["row_token"], rt)
     assert np.array_equal(got["block_expert"], be)
     assert np.array_equal(got["expert_offsets"], off)
