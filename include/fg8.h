@@ -50,6 +50,9 @@
  *     to [0, cap] (gemm_mxfp8: [0, m]).
  *   - Calls may run concurrently on different streams; a split-K workspace
  *     must not be shared by calls that can overlap.
+ *   - Every GEMM takes 128 <= k <= 2^24 - 128 with k % 128 == 0 (else
+ *     FG8_EUNSUPPORTED): the copies into LDS address a tile of up to 256
+ *     rows with 32-bit offsets.
  *   - FP32 inputs to fp8_quantize must be finite.
  */
 #ifndef FG8_H

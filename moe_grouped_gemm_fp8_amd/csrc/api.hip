@@ -29,8 +29,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
   } while (0)
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;   // row / column counts must fit int32
-constexpr int64_t kMaxK = 16384;                // sb staging covers 128 K blocks per unit
-constexpr int64_t kMaxKGrouped = ((int64_t)1 << 24) - 128;
+// 32-bit LDS-DMA offsets inside a tile of up to 256 rows: (256 - 1) * k < 2^32
+constexpr int64_t kMaxK = ((int64_t)1 << 24) - 128;
+constexpr int64_t kMaxKGrouped = kMaxK;
 
 fg8_status check_k(const char* fn, int64_t k) {
   if (k < 128 || k > kMaxK) return fail(FG8_EUNSUPPORTED, "%s: k=%lld must be in [128, %lld]", fn,

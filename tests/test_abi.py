@@ -71,7 +71,7 @@ def test_gemm_validation(L):
     assert f(ok, ok, ok, ok, ok, 0, 0, 64, 256, None, 0, None) == 1
     assert f(ok, ok, ok, ok, ok, 0, 64, 64, 200, None, 0, None) == 2
     assert f(ok, ok, ok, ok, ok, 0, 64, 64, 64, None, 0, None) == 2
-    assert f(ok, ok, ok, ok, ok, 0, 64, 64, 32768, None, 0, None) == 2
+    assert f(ok, ok, ok, ok, ok, 0, 64, 64, 1 << 24, None, 0, None) == 2
     # a split-K shape with no workspace is refused before launching
     need = L.fg8_gemm_workspace_bytes(64, 2112, 7168)
     assert need > 4096

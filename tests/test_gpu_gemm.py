@@ -59,6 +59,8 @@ CASES = [
     ("skinny_a", 7, 8192, 4096),
     ("tiny", 64, 64, 16384),                     # largest K: 128 K blocks, 8-way split-K
     ("prefill_a", 100, 392, 512),                # 64 < M <= 128 path, ragged M and N
+    ("tiny", 64, 256, 32768),                    # long K: 256 K blocks, 8-way split-K
+    ("prefill_b", 300, 256, 20480),              # long K on the 128 x 64 tiles
 ]
 
 

@@ -353,6 +353,23 @@ def test_mx_masked_small(dev, out_dtype):
             _check(d[e, :v[e]], C[e, :v[e]], S[e, :v[e]], K, f"mx expert {e}", derived=False, F=F)
 
 
+def test_mx_long_k(dev):
+    """MXFP8 with K = 32768 (1024 E8M0 blocks per row), two groups, no mask."""
+    g = np.random.default_rng(408)
+    G, m, n, K = 2, 40, 96, 32768
+    a = g.standard_normal((G, m, K)).astype(np.float32)
+    b = (g.standard_normal((G, n, K)) * K ** -0.5).astype(np.float32)
+    qa, ea = scaling.quantize_mx(a)
+    qb, eb = scaling.quantize_mx(b)
+    ta, tea, tb, teb = _gpu(qa, ea, qb, eb)
+    d = fg8.gemm_mxfp8(ta, tea, tb, teb, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    C, S = gemm.gemm_mx(qa, ea, qb, eb)
+    got = d.cpu().numpy()
+    for i in range(G):
+        check_f32(got[i], C[i], S[i], K, f"mx long K group {i}", derived=False)
+
+
 def test_mx_dense_and_exponent_spread(dev):
     """valid_rows = NULL means every row; exponents spread over a wide range
     (per-row magnitudes 2^-20 .. 2^20) exercise the E8M0 lane mapping."""
