@@ -43,7 +43,8 @@ fg8_status check_k(const char* fn, int64_t k) {
 // The kernels count work units (tiles times splits) in 32-bit integers.
 fg8_status check_units(const fg8::GemmProblem& p, const fg8::TileChoice& t, const char* fn) {
   const int64_t units = (int64_t)(p.mode == fg8::kMasked || p.mode == fg8::kKGrouped ? p.groups : 1) *
-                        ((p.M + t.bm - 1) / t.bm) * ((p.N + t.bn - 1) / t.bn) * t.splits;
+                        ((p.M + t.bm - 1) / t.bm) * ((p.N + t.bn - 1) / t.bn) * t.splits *
+                        (p.mode == fg8::kContiguous && t.bm > 128 ? 2 : 1);   // 256-row pair units
   if (units >= INT32_MAX)
     return fail(FG8_EUNSUPPORTED, "%s: %lld tiles exceed the 32-bit work-unit count", fn,
                 (long long)units);

@@ -66,6 +66,12 @@ struct Cfg {
   // split-K is compiled only into the decode-sized configurations (the large
   // tiles have no registers to spare for the partial sums)
   static constexpr bool SPLITK = WAVES == 4 && BM <= 128 && BN <= 128;
+  // PIN: the compute of each column tile is fenced off from the next
+  // (sched_barrier), so the scheduler cannot hoist every B fragment read and
+  // MFMA of the K block ahead of the promotion: the 256 x 256 tile's
+  // 128 accumulators per lane leave no room for more than two columns of
+  // partial sums in flight
+  static constexpr bool PIN = BM * BN >= 256 * 256;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
   // One stage holds KS K blocks, each laid out as: A tile | B tile | A row
@@ -141,6 +147,18 @@ __device__ __forceinline__ T uniform(T v) {
   }
 }
 
+// Fence between the column steps of a pinned configuration: neither the IR
+// passes (memory clobber) nor the machine scheduler move LDS reads or MFMAs
+// across it.
+__device__ __forceinline__ void pin_step() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// An empty asm that reads and rewrites x: the computation of x (an MFMA
+// result, a promoted accumulator) must happen before this point and cannot be
+// sunk past the branches that follow it.
+__device__ __forceinline__ void pin_value(v4f& x) { asm volatile("" : "+v"(x)); }
+
 // One MFMA operand fragment: 16 rows starting at tile row r0.
 __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int r0, int lane) {
   const int r = r0 + (lane & 15), g = lane >> 4, s = swz(r);
@@ -183,7 +201,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
   __shared__ int tile_prefix[MODE == kMasked ? 1025 : 1];
   __shared__ int flag;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: held in an SGPR, so are the LDS addresses built on it
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int wm0 = wm * C::WM, wn0 = wn * C::WN;
   const int64_t M = p.M, N = p.N, K = p.K;
@@ -235,6 +254,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
     total = tile_prefix[G];
   } else if constexpr (MODE == kKGrouped) {
     total = p.groups * (int)((M + C::BM - 1) / C::BM) * n_tiles;
+  } else if constexpr (MODE == kContiguous && C::BM == 2 * kGroup) {
+    total = 2 * (int)((M + C::BM - 1) / C::BM) * n_tiles;   // pair units, then half units
   } else {
     total = (int)((M + C::BM - 1) / C::BM) * n_tiles * splits;
   }
@@ -268,6 +289,31 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       const int k1 = min(max(p.k_offsets[w.g + 1] / kGroup, k0), KB);
       w.kb0 = k0; w.kb1 = k1; w.split = 0; w.tile = u;
       w.rows = (int)M;
+    } else if constexpr (MODE == kContiguous && C::BM == 2 * kGroup) {
+      // 256-row tiles over pairs of 128-row blocks.  A pair whose blocks
+      // belong to one expert is one unit; a pair that straddles two experts
+      // (or ends the layout) is done as two half-height units, one per block
+      // and expert, enumerated after every pair unit.  The units of the
+      // second kind for a one-expert pair are empty.
+      const int64_t mblocks = M / kGroup;
+      const int pair_units = (int)((mblocks + 1) / 2) * n_tiles;
+      const int h = u >= pair_units ? 1 : 0;
+      const int t = u - h * pair_units;
+      const int64_t b0 = 2 * (int64_t)(t / n_tiles);
+      w.n0 = (int64_t)(t % n_tiles) * C::BN;
+      const int e0 = p.block_expert[b0];
+      const int e1 = b0 + 1 < mblocks ? p.block_expert[b0 + 1] : -1;
+      if (e0 == e1 && b0 + 1 < mblocks) {
+        w.g = h == 0 ? e0 : -1;
+        w.m0 = b0 * kGroup;
+        w.rows = (int)M;
+      } else {
+        const int64_t b = b0 + h;
+        w.g = b < mblocks ? (h == 0 ? e0 : e1) : -1;
+        w.m0 = b * kGroup;
+        w.rows = (int)(w.m0 + kGroup);   // the other half's waves idle
+      }
+      w.kb0 = 0; w.kb1 = KB; w.split = 0; w.tile = u;
     } else {
       const int t = u / splits;
       w.split = u % splits;
@@ -491,7 +537,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
             for (int tm = 0; tm < C::TM; ++tm)
               acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                   fa[tm], fb, acc[tm][tn], 0, 0, 0, sA[tm], 0, sB);
+            if constexpr (C::PIN) {
+#pragma unroll
+              for (int tm = 0; tm < C::TM; ++tm) pin_value(acc[tm][tn]);
+            }
             issue_point(sub * C::TN + tn);
+            if constexpr (C::PIN) pin_step();
           }
         } else {
           // one B scale per wave (128-row blocks of B), or one per B row
@@ -538,7 +589,15 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
                   acc[tm][tn - 1][v] = fmaf(part[(tn - 1) & 1][tm][v], f, acc[tm][tn - 1][v]);
                 }
             }
+            if constexpr (C::PIN) {
+#pragma unroll
+              for (int tm = 0; tm < C::TM; ++tm) {
+                pin_value(part[tn & 1][tm]);
+                if (tn > 0) pin_value(acc[tm][tn - 1]);
+              }
+            }
             issue_point(sub * C::TN + tn);
+            if constexpr (C::PIN) pin_step();
           }
 #pragma unroll
           for (int tm = 0; tm < C::TM; ++tm)
@@ -620,32 +679,42 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       if (p.swiglu) {
         constexpr int ROW = C::BN * 4 + 16;
         static_assert(C::BN == 2 * kGroup, "one gate block and one up block per tile");
-        static_assert(C::BM * ROW <= C::STAGES * C::STAGE_BYTES, "the FP32 tile fits in LDS");
-#pragma unroll
-        for (int tm = 0; tm < C::TM; ++tm)
-#pragma unroll
-          for (int tn = 0; tn < C::TN; ++tn)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              *reinterpret_cast<float*>(smem + (wm0 + tm * 16 + 4 * (lane >> 4) + v) * ROW +
-                                        (wn0 + tn * 16 + (lane & 15)) * 4) = acc[tm][tn][v];
-        __syncthreads();
+        // rows staged at a time: whole wave row blocks that fit in the stage memory
+        constexpr int FIT = C::STAGES * C::STAGE_BYTES / ROW;
+        constexpr int CR = FIT >= C::BM ? C::BM : (FIT / C::WM) * C::WM;
+        static_assert(CR >= C::WM && C::BM % CR == 0, "the FP32 tile stages in whole wave blocks");
         const int64_t NH = N / 2;
         const int64_t hb = w.n0 / C::BN;   // 128-column block of h
         uint8_t* qo = p.q_out + w.m0 * NH + hb * kGroup;
         float* so = p.s_out + hb * M + w.m0;
         const int c = (lane & 31) * 4;
-        // two rows per wave step (lanes 0-31 and 32-63), four columns a lane
-        for (int r = wave * 2 + (lane >> 5); r < C::BM; r += 2 * C::WAVES) {
-          const float4 g = *reinterpret_cast<const float4*>(smem + r * ROW + c * 4);
-          const float4 v = *reinterpret_cast<const float4*>(smem + r * ROW + (kGroup + c) * 4);
-          const float4 h = make_float4(silu(g.x) * v.x, silu(g.y) * v.y, silu(g.z) * v.z,
-                                       silu(g.w) * v.w);
-          const float amax = group_max<32>(abs_max4(h));
-          const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
-          *reinterpret_cast<uint32_t*>(qo + r * NH + c) =
-              pack4_e4m3(make_float4(h.x / sc, h.y / sc, h.z / sc, h.w / sc));
-          if ((lane & 31) == 0) so[r] = sc;
+        const int64_t live = min((int64_t)C::BM, (int64_t)w.rows - w.m0);   // rows of this unit
+#pragma unroll
+        for (int r0 = 0; r0 < C::BM; r0 += CR) {
+          if (r0 > 0) __syncthreads();   // the previous rows have left LDS
+          if (wave_live && wm0 >= r0 && wm0 < r0 + CR) {
+#pragma unroll
+            for (int tm = 0; tm < C::TM; ++tm)
+#pragma unroll
+              for (int tn = 0; tn < C::TN; ++tn)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                  *reinterpret_cast<float*>(smem + (wm0 - r0 + tm * 16 + 4 * (lane >> 4) + v) * ROW +
+                                            (wn0 + tn * 16 + (lane & 15)) * 4) = acc[tm][tn][v];
+          }
+          __syncthreads();
+          // two rows per wave step (lanes 0-31 and 32-63), four columns a lane
+          for (int r = wave * 2 + (lane >> 5); r < CR && r0 + r < live; r += 2 * C::WAVES) {
+            const float4 g = *reinterpret_cast<const float4*>(smem + r * ROW + c * 4);
+            const float4 v = *reinterpret_cast<const float4*>(smem + r * ROW + (kGroup + c) * 4);
+            const float4 h = make_float4(silu(g.x) * v.x, silu(g.y) * v.y, silu(g.z) * v.z,
+                                         silu(g.w) * v.w);
+            const float amax = group_max<32>(abs_max4(h));
+            const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
+            *reinterpret_cast<uint32_t*>(qo + (r0 + r) * NH + c) =
+                pack4_e4m3(make_float4(h.x / sc, h.y / sc, h.z / sc, h.w / sc));
+            if ((lane & 31) == 0) so[r0 + r] = sc;
+          }
         }
         continue;   // the next unit starts with a barrier before reusing LDS
       }
@@ -728,6 +797,7 @@ using CfgS64k2 = Cfg<64, 64, 1, 4, 4, 1, 2>;   // 64 x 16
 using CfgS128k2 = Cfg<64, 128, 1, 4, 3, 1, 2>; // 64 x 32
 using CfgM32k2 = Cfg<128, 32, 4, 1, 3, 1, 2>;  // 32 x 32
 using CfgS32x2k2 = Cfg<64, 32, 2, 2, 3, 2, 2>; // 32 x 16, two workgroups per CU
+using CfgHuge8 = Cfg<256, 256, 4, 2, 2, 1, 1, true>;  // 64 x 128, two waves per SIMD
 
 struct CfgInfo {
   int bm, bn, occ;
@@ -739,13 +809,13 @@ static const CfgInfo kCfgs[] = {
     FG8_CFG_INFO(CfgS64),  FG8_CFG_INFO(CfgS128), FG8_CFG_INFO(CfgM64),  FG8_CFG_INFO(CfgM32),
     FG8_CFG_INFO(CfgBig8), FG8_CFG_INFO(CfgWide8), FG8_CFG_INFO(CfgS32k4), FG8_CFG_INFO(CfgS32k2),
     FG8_CFG_INFO(CfgS64k4), FG8_CFG_INFO(CfgS64k2), FG8_CFG_INFO(CfgS128k2), FG8_CFG_INFO(CfgM32k2),
-    FG8_CFG_INFO(CfgS32x2k2),
+    FG8_CFG_INFO(CfgS32x2k2), FG8_CFG_INFO(CfgHuge8),
 };
 #undef FG8_CFG_INFO
 enum CfgId {
   kCfgBig = 0, kCfgWide, kCfgS32, kCfgS32x2, kCfgS64, kCfgS128, kCfgM64, kCfgM32, kCfgBig8,
   kCfgWide8, kCfgS32k4, kCfgS32k2, kCfgS64k4, kCfgS64k2, kCfgS128k2, kCfgM32k2, kCfgS32x2k2,
-  kNumCfgs
+  kCfgHuge8, kNumCfgs
 };
 
 int device_cu_count() {
@@ -791,13 +861,15 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
   bool forced = false;
   int ov = -1;
   if (p.mode != kDense && tile_override(&ov, &forced_splits)) {
-    if (p.mode == kContiguous && (ov == kCfgWide || ov == kCfgWide8)) forced = true;
-    if (p.mode == kMasked && (ov == kCfgBig || ov == kCfgBig8)) forced = true;
+    if (p.mode == kContiguous && (ov == kCfgWide || ov == kCfgWide8 || ov == kCfgHuge8)) forced = true;
+    if (p.mode == kMasked && (ov == kCfgBig || ov == kCfgBig8 || ov == kCfgHuge8)) forced = true;
   }
   if (forced) {
     t.cfg = ov;
   } else if (p.mode == kContiguous) {
-    t.cfg = kCfgWide8;
+    // 256 x 256 tiles over pairs of 128-row blocks once they fill the chip:
+    // a quarter fewer operand bytes per FLOP than 128 x 256
+    t.cfg = ((p.M + 255) / 256) * ((p.N + 255) / 256) >= (int64_t)num_cus ? kCfgHuge8 : kCfgWide8;
   } else if (p.mode == kKGrouped) {
     t.cfg = kCfgBig8;
   } else if (p.mode == kDense && (forced = tile_override(&t.cfg, &forced_splits))) {
@@ -809,6 +881,9 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
     t.cfg = (p.N + 31) / 32 >= 2 * num_cus ? kCfgS128 : kCfgS32x2k2;
   } else if (p.mode == kDense && p.M <= 128) {
     t.cfg = kCfgS64k2;
+  } else if (p.mode == kDense && ((p.M + 255) / 256) * ((p.N + 255) / 256) >= (int64_t)num_cus) {
+    // enough 256 x 256 tiles for every CU: the fewest operand bytes per FLOP
+    t.cfg = kCfgHuge8;
   } else if (p.mode == kDense &&
              ((p.M + 255) / 256) * ((p.N + 127) / 128) * 3 < (int64_t)num_cus) {
     // few 256 x 128 tiles (fewer than a third of the CUs): 128 x 64 tiles
@@ -836,6 +911,7 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
       if (t.splits > kMaxSplits) t.splits = kMaxSplits;
     }
     units = tiles * t.splits;
+    if (p.mode == kContiguous && t.bm == 2 * kGroup) units *= 2;   // pair units, then half units
   }
   t.grid = (int)(units < slots ? units : slots);
   if (t.grid < 1) t.grid = 1;
@@ -884,15 +960,24 @@ hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
         case kCfgS128k2: return launch<CfgS128k2, false, kDense>(p, t.grid, s);
         case kCfgM32k2: return launch<CfgM32k2, false, kDense>(p, t.grid, s);
         case kCfgS32x2k2: return launch<CfgS32x2k2, false, kDense>(p, t.grid, s);
+        case kCfgHuge8: return launch<CfgHuge8, false, kDense>(p, t.grid, s);
         default: return launch<CfgBig, false, kDense>(p, t.grid, s);
       }
     case kContiguous:
+      if (t.cfg == kCfgHuge8) {
+        if (p.mx) return launch<CfgHuge8, true, kContiguous>(p, t.grid, s);
+        return launch<CfgHuge8, false, kContiguous>(p, t.grid, s);
+      }
       if (p.mx) return launch<CfgWide8, true, kContiguous>(p, t.grid, s);
       if (t.cfg == kCfgWide8) return launch<CfgWide8, false, kContiguous>(p, t.grid, s);
       return launch<CfgWide, false, kContiguous>(p, t.grid, s);
     case kKGrouped:
       return launch<CfgBig8, false, kKGrouped>(p, t.grid, s);
     default:
+      if (t.cfg == kCfgHuge8) {
+        if (p.mx) return launch<CfgHuge8, true, kMasked>(p, t.grid, s);
+        return launch<CfgHuge8, false, kMasked>(p, t.grid, s);
+      }
       if (t.cfg == kCfgBig8) {
         if (p.mx) return launch<CfgBig8, true, kMasked>(p, t.grid, s);
         return launch<CfgBig8, false, kMasked>(p, t.grid, s);
