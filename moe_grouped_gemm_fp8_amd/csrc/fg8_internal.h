@@ -29,6 +29,7 @@ struct GemmProblem {
   const int32_t* valid;         // masked: live rows per group (NULL = all M)
   const int32_t* k_offsets;     // K-grouped: K offset of each group [groups + 1]
   int rotate;                   // 1: start each unit's K walk at a unit-dependent block
+  int raster;                   // > 0: XCD-blocked grouped raster of the tiles, this many tile rows per group
   // contiguous only: 1 = fused SiLU-gated epilogue that writes the 1x128
   // quantization of h = silu(gate) * up (W1 rows interleaved in 128-row
   // gate/up blocks) to q_out [M][N/2] and s_out [N/256][M] instead of d
@@ -56,6 +57,7 @@ struct TileChoice {
   int splits;
   int grid;
   int rotate;
+  int raster;
 };
 
 TileChoice choose_tiles(const GemmProblem& p, int num_cus);

@@ -187,6 +187,29 @@ __device__ __forceinline__ void wait_all_memory() { asm volatile("s_waitcnt vmcn
 // x * sigmoid(x) in FP32; -0 for very negative x (e^-x overflows to inf).
 __device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
 
+// Tile order for the L2s of the eight XCDs.  A persistent grid of G
+// workgroups deals unit u to XCD u % 8; within every whole round of G units,
+// xcd_block renumbers them so that each XCD takes a contiguous run of G / 8
+// ids, and grouped_tile walks those ids down `gm` rows of tiles before moving
+// to the next column, so the tiles an XCD runs together share few A row
+// blocks and few B column blocks.  Both are bijections on [0, total).
+__device__ __forceinline__ int xcd_block(int u, int total, int G) {
+  if (G % 8) return u;
+  const int base = (u / G) * G;
+  if (base + G > total) return u;
+  const int b = u - base;
+  return base + (b % 8) * (G / 8) + b / 8;
+}
+__device__ __forceinline__ void grouped_tile(int id, int m_tiles, int n_tiles, int gm, int& mt,
+                                             int& nt) {
+  const int per = gm * n_tiles;
+  const int grp = id / per, first = grp * gm;
+  const int rows = min(m_tiles - first, gm);
+  const int r = id - grp * per;
+  mt = first + r % rows;
+  nt = r / rows;
+}
+
 struct Unit {
   int g;            // group (expert)
   int64_t m0, n0;   // tile origin inside the group
@@ -299,8 +322,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       const int pair_units = (int)((mblocks + 1) / 2) * n_tiles;
       const int h = u >= pair_units ? 1 : 0;
       const int t = u - h * pair_units;
-      const int64_t b0 = 2 * (int64_t)(t / n_tiles);
-      w.n0 = (int64_t)(t % n_tiles) * C::BN;
+      int pr = t / n_tiles, nt = t % n_tiles;
+      if (h == 0 && p.raster > 0)
+        grouped_tile(xcd_block(t, pair_units, gridDim.x), (int)((mblocks + 1) / 2), n_tiles,
+                     p.raster, pr, nt);
+      const int64_t b0 = 2 * (int64_t)pr;
+      w.n0 = (int64_t)nt * C::BN;
       const int e0 = p.block_expert[b0];
       const int e1 = b0 + 1 < mblocks ? p.block_expert[b0 + 1] : -1;
       if (e0 == e1 && b0 + 1 < mblocks) {
@@ -318,8 +345,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       const int t = u / splits;
       w.split = u % splits;
       w.tile = t;
-      w.m0 = (int64_t)(t / n_tiles) * C::BM;
-      w.n0 = (int64_t)(t % n_tiles) * C::BN;
+      int mt = t / n_tiles, nt = t % n_tiles;
+      if (splits == 1 && p.raster > 0)
+        grouped_tile(xcd_block(t, total, gridDim.x), (int)((M + C::BM - 1) / C::BM), n_tiles,
+                     p.raster, mt, nt);
+      w.m0 = (int64_t)mt * C::BM;
+      w.n0 = (int64_t)nt * C::BN;
       w.kb0 = (int)((int64_t)w.split * KB / splits);
       w.kb1 = (int)((int64_t)(w.split + 1) * KB / splits);
       w.rows = (int)M;
@@ -797,7 +828,7 @@ using CfgS64k2 = Cfg<64, 64, 1, 4, 4, 1, 2>;   // 64 x 16
 using CfgS128k2 = Cfg<64, 128, 1, 4, 3, 1, 2>; // 64 x 32
 using CfgM32k2 = Cfg<128, 32, 4, 1, 3, 1, 2>;  // 32 x 32
 using CfgS32x2k2 = Cfg<64, 32, 2, 2, 3, 2, 2>; // 32 x 16, two workgroups per CU
-using CfgHuge8 = Cfg<256, 256, 4, 2, 2, 1, 1, true>;  // 64 x 128, two waves per SIMD
+using CfgHuge8 = Cfg<256, 256, 4, 2, 2, 1, 1>;  // 64 x 128, two waves per SIMD, loads at once
 
 struct CfgInfo {
   int bm, bn, occ;
@@ -863,6 +894,7 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
   if (p.mode != kDense && tile_override(&ov, &forced_splits)) {
     if (p.mode == kContiguous && (ov == kCfgWide || ov == kCfgWide8 || ov == kCfgHuge8)) forced = true;
     if (p.mode == kMasked && (ov == kCfgBig || ov == kCfgBig8 || ov == kCfgHuge8)) forced = true;
+    if (p.mode == kKGrouped && (ov == kCfgBig8 || ov == kCfgHuge8)) forced = true;
   }
   if (forced) {
     t.cfg = ov;
@@ -871,7 +903,9 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
     // a quarter fewer operand bytes per FLOP than 128 x 256
     t.cfg = ((p.M + 255) / 256) * ((p.N + 255) / 256) >= (int64_t)num_cus ? kCfgHuge8 : kCfgWide8;
   } else if (p.mode == kKGrouped) {
-    t.cfg = kCfgBig8;
+    t.cfg = (int64_t)p.groups * ((p.M + 255) / 256) * ((p.N + 255) / 256) >= (int64_t)num_cus
+                ? kCfgHuge8
+                : kCfgBig8;
   } else if (p.mode == kDense && (forced = tile_override(&t.cfg, &forced_splits))) {
   } else if (p.mode == kDense && p.M <= 64) {
     // decode-sized M: narrow 64 x 32 tiles, two workgroups per CU (the
@@ -920,6 +954,11 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
   // block of their common A or B rows, which the L2 serves once.
   t.rotate = 0;
   if (const char* e = getenv("FG8_ROTATE")) t.rotate = atoi(e) != 0;
+  // XCD-blocked tile order, four tile rows per group, for the 256 x 256
+  // tiles (measured neutral to 4.5% faster on the dense and contiguous
+  // workloads); the other configurations keep the plain row-major order.
+  t.raster = t.cfg == kCfgHuge8 ? 4 : 0;
+  if (const char* e = getenv("FG8_RASTER")) t.raster = atoi(e) > 0 ? atoi(e) : 0;
   return t;
 }
 
@@ -941,6 +980,7 @@ static hipError_t launch(const GemmProblem& p, int grid, hipStream_t s) {
 hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
   p.splits = t.splits;
   p.rotate = t.rotate;
+  p.raster = t.raster;
   switch (p.mode) {
     case kDense:
       switch (t.cfg) {
@@ -972,6 +1012,7 @@ hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
       if (t.cfg == kCfgWide8) return launch<CfgWide8, false, kContiguous>(p, t.grid, s);
       return launch<CfgWide, false, kContiguous>(p, t.grid, s);
     case kKGrouped:
+      if (t.cfg == kCfgHuge8) return launch<CfgHuge8, false, kKGrouped>(p, t.grid, s);
       return launch<CfgBig8, false, kKGrouped>(p, t.grid, s);
     default:
       if (t.cfg == kCfgHuge8) {
