@@ -27,9 +27,15 @@
 //     (optionally split along K with a deterministic last-arriver reduction),
 //     contiguous-layout tiles whose expert comes from block_expert (with an
 //     optional gated epilogue that quantizes the activation for the next
-//     GEMM), masked-layout tiles enumerated from the device-side valid
-//     counts, or K-grouped tiles whose K range comes from per-group offsets
-//     (the weight gradient, 1x128 scales on both operands).
+//     GEMM; 256-row tiles cover pairs of 128-row blocks, and a pair that
+//     straddles two experts runs as two half-height units), masked-layout
+//     tiles enumerated from the device-side valid counts, or K-grouped tiles
+//     whose K range comes from per-group offsets (the weight gradient, 1x128
+//     scales on both operands);
+//   * the 256 x 256 tiles are dealt so that each XCD runs a compact block of
+//     them (a contiguous run of ids per XCD, walked four tile rows at a time),
+//     and their column steps are fenced so that no more than two columns of
+//     partial sums are live (the 128 accumulators per lane leave no room).
 //
 // Lane layout (measured on gfx950 by the probe tests): in the 16x16x128 MFMA
 // lane l = i + 16 g holds row i of A (column i of B) with K = 16 g .. 16 g + 15
