@@ -191,7 +191,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ void wait_all_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // x * sigmoid(x) in FP32; -0 for very negative x (e^-x overflows to inf).
-__device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
+// From the hardware exp2 and reciprocal (a few ulp each; the gated epilogue's
+// output is checked against error bounds, not bit for bit): -0 for very
+// negative x (2^(-x log2 e) overflows to inf, whose reciprocal is 0).
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
 
 // Tile order for the L2s of the eight XCDs.  A persistent grid of G
 // workgroups deals unit u to XCD u % 8; within every whole round of G units,
@@ -751,8 +756,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
                                          silu(g.w) * v.w);
             const float amax = group_max<32>(abs_max4(h));
             const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
+            const float inv = __builtin_amdgcn_rcpf(sc);   // one reciprocal per group
             *reinterpret_cast<uint32_t*>(qo + (r0 + r) * NH + c) =
-                pack4_e4m3(make_float4(h.x / sc, h.y / sc, h.z / sc, h.w / sc));
+                pack4_e4m3(make_float4(h.x * inv, h.y * inv, h.z * inv, h.w * inv));
             if ((lane & 31) == 0) so[r0 + r] = sc;
           }
         }
