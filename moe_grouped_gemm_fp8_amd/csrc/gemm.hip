@@ -915,7 +915,7 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
     t.cfg = ov;
   } else if (p.mode == kContiguous) {
     // 256 x 256 tiles over pairs of 128-row blocks once they fill the chip:
-    // a quarter fewer operand bytes per FLOP than 128 x 256
+    // a third fewer operand bytes per FLOP than 128 x 256
     t.cfg = ((p.M + 255) / 256) * ((p.N + 255) / 256) >= (int64_t)num_cus ? kCfgHuge8 : kCfgWide8;
   } else if (p.mode == kKGrouped || p.mode == kMasked) {
     // (masked: the tile count is an upper bound, every expert at capacity)
