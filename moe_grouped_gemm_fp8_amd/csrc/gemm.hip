@@ -84,7 +84,11 @@ struct Cfg {
   // scales (FP32 sa or E8M0 dwords) | B row scales (E8M0 dwords, MX only) |
   // one B-block scale per wave (FP32).
   static constexpr int A_BYTES = BM * kGroup, B_BYTES = BN * kGroup;
-  static constexpr int SA_BYTES = BM * 4, SB_BYTES = BN * 4, SBW_BYTES = 4 * WAVES;
+  // SPLITB: a wave's columns may straddle two 128-column B blocks (wave tile
+  // width not dividing 128); each wave then keeps both blocks' scales and
+  // applies them per 16-column tile
+  static constexpr bool SPLITB = (128 % (BN / WAVES_N)) != 0;
+  static constexpr int SA_BYTES = BM * 4, SB_BYTES = BN * 4, SBW_BYTES = (SPLITB ? 8 : 4) * WAVES;
   static constexpr int BLOCK_BYTES = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES + SBW_BYTES;
   static constexpr int STAGE_BYTES = KS * BLOCK_BYTES;
   // rows each wave copies per stage; one 16-byte LDS-DMA load covers 8 rows
@@ -93,7 +97,8 @@ struct Cfg {
   static_assert(A_ROWS % 8 == 0 && B_ROWS % 8 == 0, "every wave copies whole groups of 8 rows");
   static_assert(WAVES == 4 || WAVES == 8, "four or eight waves per workgroup");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be whole 16x16 MFMA tiles");
-  static_assert(WN <= 128 && (128 % WN) == 0, "a wave's columns must sit in one 128-block");
+  static_assert(WN <= 128 && ((128 % WN) == 0 || SPLITB), "a wave's columns span at most two 128-blocks");
+  static_assert(!SPLITB || WN < 128, "two B blocks per wave at most");
   static_assert(A_ROWS <= 64 && B_ROWS <= 64, "one scale load per wave must cover its rows");
   static_assert((BLOCK_BYTES - SBW_BYTES) % 16 == 0 && SBW_BYTES % 16 == 0, "aligned stage parts");
   static_assert(STAGES >= 2, "need at least double buffering");
@@ -491,6 +496,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
           const float* sbb = uniform(gsb + (int64_t)kb * N + w.n0);
           const uint32_t lb = uniform(sst + (uint32_t)(C::SA_BYTES + wave * C::B_ROWS * 4));
           if (lane < C::B_ROWS) dma4(sbb, sb_off, lb);
+        } else if constexpr (C::SPLITB) {
+          // the scales of the two B blocks this wave's columns can touch (the
+          // second clamped to the last block): lanes 0 and 1
+          const float* sbp = uniform(sb_row + kb);
+          const uint32_t lw = uniform(sst + (uint32_t)(C::SA_BYTES + C::SB_BYTES + wave * 8));
+          if (lane < 2) dma4(sbp, lane == 1 && nbw < nb_blocks - 1 ? (uint32_t)(KB * 4) : 0u, lw);
         } else {
           // this wave's B-block scale for K block kb, one lane
           const float* sbp = uniform(sb_row + kb);
@@ -592,16 +603,23 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
         } else {
           // one B scale per wave (128-row blocks of B), or one per B row
           // (K-grouped: 1x128 scales on both operands, applied per column)
+          // (a wave straddling two B blocks applies them per column tile)
+          constexpr bool PERCOL = MODE == kKGrouped || C::SPLITB;
           const float sbv =
-              MODE == kKGrouped
-                  ? 1.f
-                  : *reinterpret_cast<const float*>(Ss + C::SA_BYTES + C::SB_BYTES + wave * 4);
+              PERCOL ? 1.f
+                     : *reinterpret_cast<const float*>(Ss + C::SA_BYTES + C::SB_BYTES + wave * 4);
           float sbc[C::TN];
 #pragma unroll
-          for (int tn = 0; tn < C::TN; ++tn)
-            sbc[tn] = MODE == kKGrouped ? reinterpret_cast<const float*>(Ss + C::SA_BYTES)
-                                              [wn0 + tn * 16 + (lane & 15)]
-                                        : 1.f;
+          for (int tn = 0; tn < C::TN; ++tn) {
+            if constexpr (MODE == kKGrouped) {
+              sbc[tn] = reinterpret_cast<const float*>(Ss + C::SA_BYTES)[wn0 + tn * 16 + (lane & 15)];
+            } else if constexpr (C::SPLITB) {
+              const int blk = (int)(((w.n0 + wn0 + tn * 16) >> 7) - ((w.n0 + wn0) >> 7));
+              sbc[tn] = reinterpret_cast<const float*>(Ss + C::SA_BYTES + C::SB_BYTES + wave * 8)[blk];
+            } else {
+              sbc[tn] = 1.f;
+            }
+          }
           v4f sc[C::TM];
 #pragma unroll
           for (int tm = 0; tm < C::TM; ++tm) {
@@ -630,7 +648,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
               for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                  const float f = MODE == kKGrouped ? sc[tm][v] * sbc[tn - 1] : sc[tm][v];
+                  const float f = PERCOL ? sc[tm][v] * sbc[tn - 1] : sc[tm][v];
                   acc[tm][tn - 1][v] = fmaf(part[(tn - 1) & 1][tm][v], f, acc[tm][tn - 1][v]);
                 }
             }
@@ -648,7 +666,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
           for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-              const float f = MODE == kKGrouped ? sc[tm][v] * sbc[C::TN - 1] : sc[tm][v];
+              const float f = PERCOL ? sc[tm][v] * sbc[C::TN - 1] : sc[tm][v];
               acc[tm][C::TN - 1][v] =
                   fmaf(part[(C::TN - 1) & 1][tm][v], f, acc[tm][C::TN - 1][v]);
             }
@@ -844,6 +862,7 @@ using CfgS128k2 = Cfg<64, 128, 1, 4, 3, 1, 2>; // 64 x 32
 using CfgM32k2 = Cfg<128, 32, 4, 1, 3, 1, 2>;  // 32 x 32
 using CfgS32x2k2 = Cfg<64, 32, 2, 2, 3, 2, 2>; // 32 x 16, two workgroups per CU
 using CfgHuge8 = Cfg<256, 256, 4, 2, 2, 1, 1>;  // 64 x 128, two waves per SIMD, loads at once
+using CfgS96 = Cfg<64, 96, 2, 2, 5, 1>;          // 32 x 48, B-block scales per column tile
 
 struct CfgInfo {
   int bm, bn, occ;
@@ -855,13 +874,13 @@ static const CfgInfo kCfgs[] = {
     FG8_CFG_INFO(CfgS64),  FG8_CFG_INFO(CfgS128), FG8_CFG_INFO(CfgM64),  FG8_CFG_INFO(CfgM32),
     FG8_CFG_INFO(CfgBig8), FG8_CFG_INFO(CfgWide8), FG8_CFG_INFO(CfgS32k4), FG8_CFG_INFO(CfgS32k2),
     FG8_CFG_INFO(CfgS64k4), FG8_CFG_INFO(CfgS64k2), FG8_CFG_INFO(CfgS128k2), FG8_CFG_INFO(CfgM32k2),
-    FG8_CFG_INFO(CfgS32x2k2), FG8_CFG_INFO(CfgHuge8),
+    FG8_CFG_INFO(CfgS32x2k2), FG8_CFG_INFO(CfgHuge8), FG8_CFG_INFO(CfgS96),
 };
 #undef FG8_CFG_INFO
 enum CfgId {
   kCfgBig = 0, kCfgWide, kCfgS32, kCfgS32x2, kCfgS64, kCfgS128, kCfgM64, kCfgM32, kCfgBig8,
   kCfgWide8, kCfgS32k4, kCfgS32k2, kCfgS64k4, kCfgS64k2, kCfgS128k2, kCfgM32k2, kCfgS32x2k2,
-  kCfgHuge8, kNumCfgs
+  kCfgHuge8, kCfgS96, kNumCfgs
 };
 
 int device_cu_count() {
@@ -927,8 +946,15 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
     // decode-sized M: narrow 64 x 32 tiles, two workgroups per CU (the
     // LDS-DMA rate of a CU grows with the waves issuing), two K blocks per
     // stage, split along K; when N alone gives two waves of them, wider
-    // 64 x 128 tiles without a split
-    t.cfg = (p.N + 31) / 32 >= 2 * num_cus ? kCfgS128 : kCfgS32x2k2;
+    // tiles without a split: 64 x 96 when those fit in one round and the
+    // 64 x 128 ones would leave CUs idle (64 x 24576 x 1536: 13.7 against
+    // 14.9 us), else 64 x 128
+    if ((p.N + 31) / 32 < 2 * num_cus)
+      t.cfg = kCfgS32x2k2;
+    else if ((p.N + 95) / 96 <= num_cus && (p.N + 127) / 128 < num_cus)
+      t.cfg = kCfgS96;
+    else
+      t.cfg = kCfgS128;
   } else if (p.mode == kDense && p.M <= 128) {
     t.cfg = kCfgS64k2;
   } else if (p.mode == kDense && ((p.M + 255) / 256) * ((p.N + 255) / 256) >= (int64_t)num_cus) {
@@ -1019,6 +1045,7 @@ hipError_t launch_gemm(GemmProblem p, const TileChoice& t, hipStream_t s) {
         case kCfgM32k2: return launch<CfgM32k2, false, kDense>(p, t.grid, s);
         case kCfgS32x2k2: return launch<CfgS32x2k2, false, kDense>(p, t.grid, s);
         case kCfgHuge8: return launch<CfgHuge8, false, kDense>(p, t.grid, s);
+        case kCfgS96: return launch<CfgS96, false, kDense>(p, t.grid, s);
         default: return launch<CfgBig, false, kDense>(p, t.grid, s);
       }
     case kContiguous:

@@ -157,3 +157,16 @@ def test_abi_errors_do_not_launch(dev):
             fg8._lib._ptr(a), fg8._lib._ptr(a), fg8._lib._ptr(a), fg8._lib._ptr(a),
             fg8._lib._ptr(a), 0, 64, 64, 200, None, 0, None))
     assert e.value.status == fg8._lib.FG8_EUNSUPPORTED and "multiple of 128" in str(e.value)
+
+
+@pytest.mark.parametrize("name,M,N,K", [
+    ("skinny_a", 64, 2112, 7168),    # 48-column wave tiles straddle 128-column B blocks
+    ("tiny", 17, 130, 256),          # ragged N, one partial B block
+    ("prefill_b", 300, 1000, 1024),  # several tiles in M, split-K
+])
+def test_dense_64x96_tiles(dev, monkeypatch, name, M, N, K):
+    """The 64 x 96 configuration (index 18 of the compiled list, forced by the
+    tuning hook): each wave keeps the scales of both 128-column B blocks its
+    columns can touch and applies them per 16-column tile."""
+    monkeypatch.setenv("FG8_TILE_OVERRIDE", "18")
+    test_dense_parity(dev, name, M, N, K, torch.bfloat16)
