@@ -86,6 +86,19 @@ def test_dense_prefill_full_size_sampled_rows(dev):
     check_bf16(d[rows], C, S, 2048, "prefill full size", S_flush=F)
 
 
+def test_dense_256_tiles_under_one_round_sampled_rows(dev):
+    """4096 x 2112 x 7168: 144 tiles of 256 x 256, fewer than the CUs, are
+    chosen over 272 tiles of 256 x 128 (which would need a second round);
+    the oracle computes 160 sampled rows of the default launch."""
+    A, B = inputs.dense_case("prefill_b", 4096, 2112, 7168)
+    qa, sa, qb, sb = _quantized(A, B)
+    d = _run(qa, sa, qb, sb, torch.bfloat16)
+    rows = np.unique(np.concatenate([np.arange(0, 4096, 32), [1, 255, 256, 4095],
+                                     np.random.default_rng(302).choice(4096, 28)]))
+    C, S, F = ref_blockscaled(qa[rows], sa[:, rows], qb, sb)
+    check_bf16(d[rows], C, S, 7168, "4096x2112x7168 sampled", S_flush=F)
+
+
 def test_quantize_then_gemm_on_gpu(dev):
     """The activation path as the benchmark runs it: the GPU quantizes A and
     B, the GEMM consumes them; the oracle quantizes and multiplies on its own."""
@@ -163,10 +176,13 @@ def test_abi_errors_do_not_launch(dev):
     ("skinny_a", 64, 2112, 7168),    # 48-column wave tiles straddle 128-column B blocks
     ("tiny", 17, 130, 256),          # ragged N, one partial B block
     ("prefill_b", 300, 1000, 1024),  # several tiles in M, split-K
+    ("skinny_a", 64, 2112, 1152),    # 9 K blocks: the last stage holds one
+    ("tiny", 17, 130, 640),          # 5 K blocks, ragged M and N
 ])
 def test_dense_64x96_tiles(dev, monkeypatch, name, M, N, K):
     """The 64 x 96 configuration (index 18 of the compiled list, forced by the
     tuning hook): each wave keeps the scales of both 128-column B blocks its
-    columns can touch and applies them per 16-column tile."""
+    columns can touch and applies them per 16-column tile; two K blocks per
+    stage, so an odd number of K blocks leaves the last stage half used."""
     monkeypatch.setenv("FG8_TILE_OVERRIDE", "18")
     test_dense_parity(dev, name, M, N, K, torch.bfloat16)
