@@ -237,6 +237,16 @@ struct Unit {
 template <class C, bool MX, int MODE>
 __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGES * C::STAGE_BYTES];
+  // MXG: the E8M0 scales of the two-stage tiles are fetched for four K blocks
+  // at a time (16 bytes per tile row) into two alternating group buffers,
+  // [row: BM A rows, then BN B rows][4 dwords, one per K block], instead of
+  // one dword per row and K block: a quarter of the scale loads, each
+  // touching 16 rows instead of 32.
+  constexpr bool MXG = MX && C::STAGES == 2;
+  constexpr int GRP_DWORDS = (C::BM + C::BN) * 4;
+  static_assert(!MXG || (!C::SPLITK && C::KS == 1 && C::A_ROWS % 16 == 0 && C::B_ROWS % 16 == 0),
+                "grouped E8M0 scales: whole K ranges, one K block per stage, 16-row loads");
+  __shared__ __attribute__((aligned(16))) uint32_t mx_grp[MXG ? 2 * GRP_DWORDS : 1];
   __shared__ int tile_prefix[MODE == kMasked ? 1025 : 1];
   __shared__ int flag;
 
@@ -301,6 +311,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
 
   v4f acc[C::TM][C::TN];
   const uint32_t lds0 = lds_addr(smem);
+  const uint32_t mxg0 = lds_addr(mx_grp);
 
   for (int u = blockIdx.x; u < total; u += gridDim.x) {
     // ---- decode the unit
@@ -452,6 +463,22 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
         sb_off = (uint32_t)(((rb < N - 1 ? rb : N - 1) - w.n0) * 4);
       }
     }
+    // MXG: lane l fetches dword (l & 3) of row (l >> 2) of each 16-row slice
+    // of this wave's A and B rows; the K block index is clamped at the end of
+    // the row (a partial last group), so every byte read lies in the row.
+    uint32_t ga_off[MXG ? C::A_ROWS / 16 : 1], gb_off[MXG ? C::B_ROWS / 16 : 1];
+    if constexpr (MXG) {
+#pragma unroll
+      for (int c = 0; c < C::A_ROWS / 16; ++c) {
+        const int64_t r = w.m0 + wave * C::A_ROWS + 16 * c + (lane >> 2);
+        ga_off[c] = (uint32_t)(((r < last_row ? r : last_row) - w.m0) * (K / kMxBlock));
+      }
+#pragma unroll
+      for (int c = 0; c < C::B_ROWS / 16; ++c) {
+        const int64_t r = w.n0 + wave * C::B_ROWS + 16 * c + (lane >> 2);
+        gb_off[c] = (uint32_t)(((r < N - 1 ? r : N - 1) - w.n0) * (K / kMxBlock));
+      }
+    }
     // the B-block scale row of this wave's columns (FP32 path)
     const int64_t nbw0 = (w.n0 + wn0) / kGroup;
     const int64_t nbw = nbw0 < nb_blocks - 1 ? nbw0 : nb_blocks - 1;
@@ -476,7 +503,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
         dma16(bb, b_off[i],
               uniform(st + (uint32_t)(C::A_BYTES + (wave * C::B_ROWS + i * 8) * kGroup)));
       } else if (r == C::A_LOADS + C::B_LOADS) {
-        if constexpr (MX) {
+        if constexpr (MXG) {
+          // the group of K blocks kb .. kb + 3, issued with its first block
+          if ((kb & 3) != 0) return;
+          const uint32_t kd = (uint32_t)min(kb + (lane & 3), KB - 1) * 4;
+          const uint8_t* eab = uniform(gea + w.m0 * (K / kMxBlock));
+          const uint32_t gl = uniform(mxg0 + (uint32_t)(((kb >> 2) & 1) * GRP_DWORDS * 4));
+#pragma unroll
+          for (int c = 0; c < C::A_ROWS / 16; ++c)
+            dma4(eab, ga_off[c] + kd, uniform(gl + (uint32_t)((wave * C::A_ROWS + 16 * c) * 16)));
+        } else if constexpr (MX) {
           // E8M0 bytes of K block kb for each tile row: one dword per row
           const uint8_t* eab = uniform(gea + w.m0 * (K / kMxBlock) + kb * 4);
           const uint32_t la = uniform(sst + (uint32_t)(wave * C::A_ROWS * 4));
@@ -487,7 +523,16 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
           if (lane < C::A_ROWS) dma4(sab, sa_off, la);
         }
       } else {
-        if constexpr (MX) {
+        if constexpr (MXG) {
+          if ((kb & 3) != 0) return;
+          const uint32_t kd = (uint32_t)min(kb + (lane & 3), KB - 1) * 4;
+          const uint8_t* ebb = uniform(geb + w.n0 * (K / kMxBlock));
+          const uint32_t gl = uniform(mxg0 + (uint32_t)(((kb >> 2) & 1) * GRP_DWORDS * 4));
+#pragma unroll
+          for (int c = 0; c < C::B_ROWS / 16; ++c)
+            dma4(ebb, gb_off[c] + kd,
+                 uniform(gl + (uint32_t)((C::BM + wave * C::B_ROWS + 16 * c) * 16)));
+        } else if constexpr (MX) {
           const uint8_t* ebb = uniform(geb + w.n0 * (K / kMxBlock) + kb * 4);
           const uint32_t lb = uniform(sst + (uint32_t)(C::SA_BYTES + wave * C::B_ROWS * 4));
           if (lane < C::B_ROWS) dma4(ebb, sb_off, lb);
@@ -526,7 +571,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
     // tiles that run at the same time and share an operand (the A rows of a
     // skinny GEMM, the A tile of a row of output tiles) then read different
     // K blocks of it instead of all hitting the same L2 lines at once.
-    const int rot = p.rotate && nkb > 0 ? uniform(u % nkb) : 0;
+    const int rot = p.rotate && nkb > 0 && !MXG ? uniform(u % nkb) : 0;   // MXG: groups in order
     auto kb_of = [&](int j) {
       const int x = j + rot;
       return w.kb0 + (x >= nkb ? x - nkb : x);
@@ -579,16 +624,21 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
 #pragma unroll
         for (int tm = 1; tm < C::TM; ++tm) fa[tm] = load_frag(As, wm0 + tm * 16, lane);
         if constexpr (MX) {
+          // the dword of K block kb of each row: per-stage, or in its group buffer
+          const int kbc = kb_of(si * C::KS + sub);
+          const uint32_t* sa_w = MXG ? mx_grp + ((kbc >> 2) & 1) * GRP_DWORDS + (kbc & 3)
+                                     : reinterpret_cast<const uint32_t*>(Ss);
+          const uint32_t* sb_w = MXG ? sa_w + C::BM * 4
+                                     : reinterpret_cast<const uint32_t*>(Ss + C::SA_BYTES);
+          constexpr int RS = MXG ? 4 : 1;   // dwords per row
           int sA[C::TM];
 #pragma unroll
           for (int tm = 0; tm < C::TM; ++tm)
-            sA[tm] = (int)(reinterpret_cast<const uint32_t*>(Ss)[wm0 + tm * 16 + (lane & 15)] >>
-                           (8 * (lane >> 4)));
+            sA[tm] = (int)(sa_w[(wm0 + tm * 16 + (lane & 15)) * RS] >> (8 * (lane >> 4)));
 #pragma unroll
           for (int tn = 0; tn < C::TN; ++tn) {
             const v8i fb = tn == 0 ? fb0 : load_frag(Bs, wn0 + tn * 16, lane);
-            const int sB = (int)(reinterpret_cast<const uint32_t*>(Ss + C::SA_BYTES)
-                                     [wn0 + tn * 16 + (lane & 15)] >> (8 * (lane >> 4)));
+            const int sB = (int)(sb_w[(wn0 + tn * 16 + (lane & 15)) * RS] >> (8 * (lane >> 4)));
 #pragma unroll
             for (int tm = 0; tm < C::TM; ++tm)
               acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(

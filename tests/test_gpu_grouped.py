@@ -332,8 +332,8 @@ def test_masked_full_size_sampled(dev):
 
 # ------------------------------------------------------------- MXFP8
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_mx_masked_small(dev, out_dtype):
-    E, cap, N, K = 5, 80, 160, 384
+def test_mx_masked_small(dev, out_dtype, K=384):
+    E, cap, N = 5, 80, 160
     valid = [80, 0, 33, 1, 79]
     v, a, b = _masked_inputs(E, cap, N, K, workload=42, valid=valid)
     qa, ea = scaling.quantize_mx(a)

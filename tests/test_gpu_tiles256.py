@@ -55,6 +55,13 @@ def test_masked(dev, tiles256, out_dtype):
     G.test_mx_masked_small(dev, out_dtype)
 
 
+@pytest.mark.parametrize("K", [640, 1152, 2048])
+def test_mx_masked_scale_groups(dev, tiles256, K):
+    """The 256 x 256 MXFP8 tiles fetch E8M0 scales for four K blocks at a
+    time: 5 and 9 K blocks end on a partial group, 16 on whole ones."""
+    G.test_mx_masked_small(dev, torch.float32, K=K)
+
+
 def test_masked_clamped_counts(dev, tiles256):
     G.test_masked_counts_are_clamped(dev)
 
