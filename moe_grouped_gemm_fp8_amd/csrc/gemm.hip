@@ -240,8 +240,8 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
   // MXG: the E8M0 scales of the two-stage tiles are fetched for four K blocks
   // at a time (16 bytes per tile row) into two alternating group buffers,
   // [row: BM A rows, then BN B rows][4 dwords, one per K block], instead of
-  // one dword per row and K block: a quarter of the scale loads, each
-  // touching 16 rows instead of 32.
+  // one dword per row and K block: half the scale loads, each touching 16
+  // rows instead of 32, so a quarter of the cache lines.
   constexpr bool MXG = MX && C::STAGES == 2;
   constexpr int GRP_DWORDS = (C::BM + C::BN) * 4;
   static_assert(!MXG || (!C::SPLITK && C::KS == 1 && C::A_ROWS % 16 == 0 && C::B_ROWS % 16 == 0),
