@@ -35,7 +35,8 @@ def _run(x, kind):
     return q.cpu().numpy(), s.cpu().numpy()
 
 
-@pytest.mark.parametrize("shape", [(1, 128), (37, 384), (3, 130, 256), (64, 7168)])
+# (2, 8200, 512): enough rows for one wave per whole row, in a batch of two
+@pytest.mark.parametrize("shape", [(1, 128), (37, 384), (3, 130, 256), (64, 7168), (2, 8200, 512)])
 def test_1x128_bit_exact(dev, shape):
     x = _hard_values(np.random.default_rng(200), shape)
     q, s = _run(x, "1x128")
