@@ -43,6 +43,12 @@ def test_contiguous(dev, tiles256, shape, out_dtype):
     G.test_contiguous_mx_small(dev, shape, out_dtype)
 
 
+def test_contiguous_mx_partial_scale_group(dev, tiles256):
+    """K = 640: five K blocks, so the E8M0 scales end on a partial group of
+    the four fetched at a time."""
+    G.test_contiguous_mx_small(dev, (300, 640, 384, 6, 2), torch.float32)
+
+
 def test_contiguous_skipped_blocks(dev, tiles256):
     G.test_contiguous_zero_expert_and_padding(dev)
     G.test_contiguous_out_of_range_expert_ids_skip_their_block(dev)
