@@ -313,6 +313,17 @@ fg8_status moe_contiguous_layout_fp8(const void* x, int32_t x_is_bf16, int64_t t
  * expert, rounded up to whole 128-row blocks (0 for arguments out of range). */
 int64_t fg8_moe_capacity(int64_t tokens, int32_t topk, int32_t num_experts);
 
+/* Diagnostic, host only (no GPU call): the tiling the library picks for a
+ * GEMM of this shape on a device with num_cus compute units.  mode: 0 dense
+ * (gemm_fp8_blockscaled; m, n, k as there), 1 contiguous (m = m_total),
+ * 2 masked (m = cap, groups = experts), 3 K-grouped (m, n as the output,
+ * k = total rows, groups = number of groups).  Writes out[0..4] = tile rows,
+ * tile columns, K splits, workgroups launched, and the tile-order group size
+ * (0: plain order).  FG8_EINVAL for a NULL out, an unknown mode, sizes < 1,
+ * k not a positive multiple of 128, or num_cus < 1. */
+fg8_status fg8_tile_choice(int32_t mode, int64_t m, int64_t n, int64_t k, int32_t groups,
+                           int32_t num_cus, int32_t* out);
+
 /* Text of the calling thread's last non-OK status ("" if none). */
 const char* fg8_last_error(void);
 

@@ -44,6 +44,7 @@ _SIGNATURES = {
                                   _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr],
     "fg8_moe_capacity": [_c_i64, _c_i32, _c_i32],
     "fg8_gemm_workspace_bytes": [_c_i64, _c_i64, _c_i64],
+    "fg8_tile_choice": [_c_i32, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _c_ptr],
     "fg8_last_error": [],
     "fg8_version": [],
 }

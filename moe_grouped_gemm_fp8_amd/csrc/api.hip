@@ -331,6 +331,21 @@ fg8_status grouped_gemm_mxfp8_contiguous(const uint8_t* a, const uint8_t* sa_e8m
   return run(p, fn, stream);
 }
 
+fg8_status fg8_tile_choice(int32_t mode, int64_t m, int64_t n, int64_t k, int32_t groups,
+                           int32_t num_cus, int32_t* out) {
+  if (!out) return fail(FG8_EINVAL, "fg8_tile_choice: out is NULL");
+  if (mode < fg8::kDense || mode > fg8::kKGrouped || m < 1 || n < 1 || k < 128 || k % 128 ||
+      groups < 1 || num_cus < 1)
+    return fail(FG8_EINVAL, "fg8_tile_choice: bad arguments (mode=%d m=%lld n=%lld k=%lld "
+                "groups=%d num_cus=%d)", (int)mode, (long long)m, (long long)n, (long long)k,
+                (int)groups, (int)num_cus);
+  fg8::GemmProblem p{};
+  p.mode = (int)mode; p.M = m; p.N = n; p.K = k; p.groups = groups;
+  const fg8::TileChoice t = fg8::choose_tiles(p, num_cus);
+  out[0] = t.bm; out[1] = t.bn; out[2] = t.splits; out[3] = t.grid; out[4] = t.raster;
+  return FG8_OK;
+}
+
 int64_t fg8_moe_capacity(int64_t tokens, int32_t topk, int32_t num_experts) {
   if (tokens < 1 || tokens >= kMaxDim || topk < 1 || topk > 256 || num_experts < 1 ||
       num_experts > 1024)
