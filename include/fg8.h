@@ -225,8 +225,11 @@ fg8_status grouped_gemm_mxfp8_contiguous(const uint8_t* a, const uint8_t* sa_e8m
  *   silu(x) = x / (1 + e^-x),   G = the contiguous product A W1^T in FP32,
  * i.e. the rows of W1 (and of its 128x128 scales) interleave in 128-row
  * blocks: gate block j at rows 256 j .. 256 j + 127, up block j at rows
- * 256 j + 128 .. 256 j + 255.  h is quantized 1x128 exactly as fp8_quantize
- * does it (from the FP32 h the kernel computes):
+ * 256 j + 128 .. 256 j + 255.  In FP32, silu(g) = g * rcp(1 + exp2(-g log2 e))
+ * from the hardware exp2 and reciprocal (within a few FP32 ulp of the exact
+ * value), and h = silu(g) * u.  That FP32 h is then quantized 1x128 by the
+ * rule of fp8_quantize, bit for bit: s = fl32(amax / 448) (1 when the group
+ * is all zero) and q = e4m3(fl32(h / s)), both correctly rounded divisions.
  *   a, sa, b [E][n][k], sb [E][n/128][k/128], block_expert: as
  *            grouped_gemm_fp8_contiguous (b interleaved as above)
  *   q_out    uint8 [m_total][n/2]       s_out  float [n/256][m_total]

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is written by the LDS-DMA asm
+
 namespace fg8 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -73,5 +75,78 @@ struct RowVec<uint16_t> {   // BF16 bits widen exactly to FP32
     }
   }
 };
+
+// ---------------------------------------------------------------- GEMM helpers
+// 16-byte chunk swizzle of LDS row r.  Measured with SQ_LDS_BANK_CONFLICT on
+// gfx950: (r >> 1) & 7 leaves the MFMA operand reads (one chunk of 16
+// consecutive rows per ds_read_b128) free of bank conflicts.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Global -> LDS copies without staging registers (global_load_lds_*).
+// Lane i of the wave writes its 16 (or 4) bytes at LDS address m0 + 16 i
+// (4 i); the global address is the uniform base plus the lane's 32-bit
+// offset.  They are issued from inline assembly so that the compiler does not
+// guard every later LDS read with a wait for all of them: the kernel counts
+// these loads itself (wait_vmcnt) and orders LDS use with barriers.  The
+// instructions write no VGPR.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+template <class T>
+__device__ __forceinline__ T uniform(T v) {
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  } else {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+  }
+}
+
+// One MFMA operand fragment: 16 rows starting at tile row r0.
+__device__ __forceinline__ v8i load_frag(const uint8_t* tile, int r0, int lane) {
+  const int r = r0 + (lane & 15), g = lane >> 4, s = swz(r);
+  const uint8_t* row = tile + r * kGroup;
+  const int4 lo = *reinterpret_cast<const int4*>(row + ((g ^ s) << 4));
+  const int4 hi = *reinterpret_cast<const int4*>(row + (((g + 4) ^ s) << 4));
+  v8i f;
+  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
+  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
+  return f;
+}
+
+// Split-K partials are published with 16-byte buffer stores that carry the
+// agent-scope coherence bit (sc1: written through to the point of coherence
+// shared by all XCDs) and read back with sc1 buffer loads; a vmcnt(0) wait
+// orders them before the arrival counter, so no L2 write-back is needed.
+// Raw buffer descriptor: base, byte bound, no stride, gfx9 dword 3.
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kCoherent = 16;   // cache-policy operand of the buffer builtins: sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferDword3);
+}
+__device__ __forceinline__ void wait_all_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace fg8

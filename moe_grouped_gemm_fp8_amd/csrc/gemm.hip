@@ -50,14 +50,7 @@
 #include "fg8_device.h"
 #include "fg8_internal.h"
 
-#pragma clang diagnostic ignored "-Winline-asm"   // m0 is written by the LDS-DMA asm
-
 namespace fg8 {
-
-// 16-byte chunk swizzle of LDS row r.  Measured with SQ_LDS_BANK_CONFLICT on
-// gfx950: (r >> 1) & 7 leaves the MFMA operand reads (one chunk of 16
-// consecutive rows per ds_read_b128) free of bank conflicts.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_, int OCC_, int KS_ = 1,
           bool SPREAD_ = false>
@@ -105,14 +98,6 @@ struct Cfg {
   static_assert(STAGE_BYTES % 16 == 0, "stages stay 16-byte aligned");
 };
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 template <int L, int MAXN>
 __device__ __forceinline__ void wait_stages_after(int pending) {
   // Wait until at most `pending` later stages (L loads each) are outstanding.
@@ -121,40 +106,6 @@ __device__ __forceinline__ void wait_stages_after(int pending) {
   } else {
     if (pending >= MAXN) wait_vmcnt<L * MAXN>();
     else wait_stages_after<L, MAXN - 1>(pending);
-  }
-}
-
-// Global -> LDS copies without staging registers (global_load_lds_*).
-// Lane i of the wave writes its 16 (or 4) bytes at LDS address m0 + 16 i
-// (4 i); the global address is the uniform base plus the lane's 32-bit
-// offset.  They are issued from inline assembly so that the compiler does not
-// guard every later LDS read with a wait for all of them: the kernel counts
-// these loads itself (wait_vmcnt) and orders LDS use with barriers.  The
-// instructions write no VGPR.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
-}
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
-}
-template <class T>
-__device__ __forceinline__ T uniform(T v) {
-  if constexpr (sizeof(T) == 8) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, v);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
-    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
-  } else {
-    return __builtin_bit_cast(T, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
   }
 }
 
@@ -170,35 +121,10 @@ __device__ __forceinline__ void pin_step() {
 // sunk past the branches that follow it.
 __device__ __forceinline__ void pin_value(v4f& x) { asm volatile("" : "+v"(x)); }
 
-// One MFMA operand fragment: 16 rows starting at tile row r0.
-__device__ __forceinline__ v8i load_frag(const uint8_t* tile, int r0, int lane) {
-  const int r = r0 + (lane & 15), g = lane >> 4, s = swz(r);
-  const uint8_t* row = tile + r * kGroup;
-  const int4 lo = *reinterpret_cast<const int4*>(row + ((g ^ s) << 4));
-  const int4 hi = *reinterpret_cast<const int4*>(row + (((g + 4) ^ s) << 4));
-  v8i f;
-  f[0] = lo.x; f[1] = lo.y; f[2] = lo.z; f[3] = lo.w;
-  f[4] = hi.x; f[5] = hi.y; f[6] = hi.z; f[7] = hi.w;
-  return f;
-}
-
-// Split-K partials are published with 16-byte buffer stores that carry the
-// agent-scope coherence bit (sc1: written through to the point of coherence
-// shared by all XCDs) and read back with sc1 buffer loads; a vmcnt(0) wait
-// orders them before the arrival counter, so no L2 write-back is needed.
-// Raw buffer descriptor: base, byte bound, no stride, gfx9 dword 3.
-constexpr int kBufferDword3 = 0x00020000;
-constexpr int kCoherent = 16;   // cache-policy operand of the buffer builtins: sc1
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferDword3);
-}
-__device__ __forceinline__ void wait_all_memory() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// x * sigmoid(x) in FP32; -0 for very negative x (e^-x overflows to inf).
-// From the hardware exp2 and reciprocal (a few ulp each; the gated epilogue's
-// output is checked against error bounds, not bit for bit): -0 for very
-// negative x (2^(-x log2 e) overflows to inf, whose reciprocal is 0).
+// x * sigmoid(x) in FP32 from the hardware exp2 and reciprocal (each within
+// a few ulp, so silu is within a few FP32 ulp of its correctly rounded
+// value); -0 for very negative x (2^(-x log2 e) overflows to inf, whose
+// reciprocal is 0).
 __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
 }
@@ -823,10 +749,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
             const float4 h = make_float4(silu(g.x) * v.x, silu(g.y) * v.y, silu(g.z) * v.z,
                                          silu(g.w) * v.w);
             const float amax = group_max<32>(abs_max4(h));
+            // the 1x128 rule of fp8_quantize: s = amax / 448 and codes of
+            // h / s, both correctly rounded FP32 divisions
             const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
-            const float inv = __builtin_amdgcn_rcpf(sc);   // one reciprocal per group
             *reinterpret_cast<uint32_t*>(qo + (r0 + r) * NH + c) =
-                pack4_e4m3(make_float4(h.x * inv, h.y * inv, h.z * inv, h.w * inv));
+                pack4_e4m3(make_float4(h.x / sc, h.y / sc, h.z / sc, h.w / sc));
             if ((lane & 31) == 0) so[r0 + r] = sc;
           }
         }
