@@ -1,9 +1,9 @@
 """Seeded synthetic inputs for the fine-grained FP8 GEMM workloads.
 
-This module is shared by the tests, the benchmark and the oracle's callers.
-It holds no arithmetic of the method (no scaling, no quantization, no GEMM):
-only FP32 source tensors, MoE routing and the row layout that the grouped
-GEMMs consume.  Every draw uses numpy's PCG64 generator seeded with
+This module is shared by the tests and the benchmark.  It holds no
+arithmetic of the method (no scaling, no quantization, no GEMM, no routing
+layout): only FP32 source tensors, the router's top-k expert ids and the
+masked layout's counts.  Every draw uses numpy's PCG64 generator seeded with
 [workload id, stream], stream 0 = A, 1 = B, 2 = row modifiers, 3 = routing
 or counts, 4 = second weight set, 5 = second activation set.
 
@@ -14,7 +14,7 @@ masked layouts from the DeepGEMM release news, ctol-kr.com, section 4):
   1  skinny dense: A = z * r_m with ln r_m ~ U(ln 0.01, ln 10); B ~ N(0, 1/K)
   2  prefill dense: A = z * |t_m| with t_m ~ Student-t(3) per row; B ~ N(0, 1/K)
   3  MoE contiguous: tokens pick top-k distinct experts with Zipf(1.1)
-     popularity; rows grouped per expert in token order, padded to 128
+     popularity (the layout itself is the routing step's output)
   4  MoE masked: per-expert valid counts ~ U{0..cap}; rows past the count are
      junk (finite here; tests poison the quantized copies)
 """
@@ -23,9 +23,6 @@ from __future__ import annotations
 from dataclasses import dataclass
 
 import numpy as np
-
-ROW_BLOCK = 128
-
 
 def rng(workload: int, stream: int) -> np.random.Generator:
     return np.random.default_rng([workload, stream])
@@ -106,47 +103,6 @@ def zipf_topk_routing(workload: int, tokens: int, experts: int, topk: int,
 
 
 @dataclass
-class ContiguousLayout:
-    """Rows of all experts stacked, each expert padded to a multiple of 128."""
-    row_token: np.ndarray      # [M_pad] int64, source token of each row, -1 = padding
-    block_expert: np.ndarray   # [M_pad / 128] int32, expert of each 128-row block
-    counts: np.ndarray         # [E] int64 routed rows per expert (before padding)
-
-    @property
-    def m_total(self) -> int:
-        return int(self.row_token.shape[0])
-
-    @property
-    def valid_rows(self) -> int:
-        return int(self.counts.sum())
-
-
-def contiguous_layout(routing: np.ndarray, experts: int) -> ContiguousLayout:
-    """Group routed (token, expert) pairs per expert in ascending token order
-    and pad each expert's rows to a multiple of 128."""
-    tokens = routing.shape[0]
-    rows, blocks, counts = [], [], np.zeros(experts, np.int64)
-    tok_ids = np.arange(tokens)
-    for e in range(experts):
-        toks = tok_ids[(routing == e).any(axis=1)]
-        counts[e] = toks.size
-        nblk = -(-toks.size // ROW_BLOCK)
-        pad = nblk * ROW_BLOCK - toks.size
-        rows.append(np.concatenate([toks, np.full(pad, -1)]))
-        blocks.append(np.full(nblk, e, np.int32))
-    return ContiguousLayout(np.concatenate(rows).astype(np.int64),
-                            np.concatenate(blocks).astype(np.int32), counts)
-
-
-def gather_rows(x: np.ndarray, row_token: np.ndarray) -> np.ndarray:
-    """Stack x[row_token] with zero rows for padding (-1)."""
-    out = np.zeros((row_token.shape[0], x.shape[1]), dtype=x.dtype)
-    live = row_token >= 0
-    out[live] = x[row_token[live]]
-    return out
-
-
-@dataclass
 class ContiguousCase:
     tokens: int = 8192
     hidden: int = 7168       # K of the first expert GEMM, N of the second
@@ -157,20 +113,22 @@ class ContiguousCase:
     workload: int = 3
 
 
-def contiguous_case(c: ContiguousCase):
-    """Inputs of both expert GEMMs in the contiguous layout:
-    (layout, A1 [M_pad, hidden], W1 [E, inter, hidden], A2 [M_pad, inter2],
-    W2 [E, hidden, inter2]); padding rows of A1 and A2 are zero."""
-    routing = zipf_topk_routing(c.workload, c.tokens, c.experts, c.topk)
-    lay = contiguous_layout(routing, c.experts)
+def contiguous_sources(c: ContiguousCase):
+    """The FP32 sources of the contiguous MoE workload: (topk ids [tokens,
+    topk] int32, token rows x [tokens, hidden], W1 [E, inter, hidden],
+    W2 [E, hidden, inter2]).  The row layout the grouped GEMM consumes is
+    built from the ids by the method's routing step, not here."""
+    ids = zipf_topk_routing(c.workload, c.tokens, c.experts, c.topk)
     x = _normal(rng(c.workload, 0), (c.tokens, c.hidden))
-    a1 = gather_rows(x, lay.row_token)
-    del x
     w1 = _normal(rng(c.workload, 1), (c.experts, c.inter, c.hidden), c.hidden ** -0.5)
-    a2 = _normal(rng(c.workload, 5), (lay.m_total, c.inter2))
-    a2[lay.row_token < 0] = 0.0
     w2 = _normal(rng(c.workload, 4), (c.experts, c.hidden, c.inter2), c.inter2 ** -0.5)
-    return lay, a1, w1, a2, w2
+    return ids, x, w1, w2
+
+
+def contiguous_a2(c: ContiguousCase, rows: int):
+    """The second expert GEMM's FP32 input, N(0, 1), one row per layout row
+    (the caller zeroes the padding rows)."""
+    return _normal(rng(c.workload, 5), (rows, c.inter2))
 
 
 @dataclass

@@ -7,9 +7,9 @@ import pytest
 import torch
 
 import moe_grouped_gemm_fp8_amd as fg8
-from moe_grouped_gemm_fp8_amd import inputs
+import inputs
 from oracle import backward, routing
-from parity import check_bf16, check_f32, ref_kgrouped
+from parity import TruncRows, check_bf16, check_f32, ref_blockscaled, ref_kgrouped
 from test_gpu_quantize import _hard_values
 
 pytestmark = pytest.mark.gpu
@@ -123,3 +123,107 @@ def test_wgrad_from_the_routing_layout_full_size_sampled(dev):
         C, S, F = ref_kgrouped(qa_o, sa_o, qb_o, sb_o, [0, k1 - k0])
         got = d[e, ib * 128:(ib + 1) * 128, jb * 128:(jb + 1) * 128].cpu().numpy()
         check_f32(got, C[0], S[0], k1 - k0, f"expert {e} block ({ib}, {jb})", S_flush=F[0])
+
+
+def _dx_rows(qdy, sdy, qw, sw):
+    """Oracle dX = dY W for rows of one expert: dY [rows, N_out] 1x128-
+    dequantized, W [N_out, K_in] 128x128-dequantized, multiplied as they are
+    (no transpose); returns (C, S) [rows, K_in]."""
+    from oracle import gemm
+    dY = gemm.dequant_1x128(qdy, sdy)
+    W = gemm.dequant_128x128(qw, sw)
+    return dY @ W, np.abs(dY) @ np.abs(W)
+
+
+def _dx_reference(qdy, sdy, qw, sw, block_expert):
+    """_dx_rows over the contiguous layout, plus the S_trunc term of the
+    GPU's product (dY times the transposed weight)."""
+    rows_e = np.repeat(np.asarray(block_expert), 128)
+    C = np.zeros((qdy.shape[0], qw.shape[2]))
+    S = np.zeros_like(C)
+    F = TruncRows(C.shape)
+    for e in range(qw.shape[0]):
+        r = rows_e == e
+        if r.any():
+            C[r], S[r] = _dx_rows(qdy[r], sdy[:, r], qw[e], sw[e])
+            F[r] = ref_blockscaled(qdy[r], sdy[:, r], np.ascontiguousarray(qw[e].T),
+                                   np.ascontiguousarray(sw[e].T))[2]
+    return C, S, F
+
+
+def _transposed_weight(qw, sw):
+    """W^T per expert: codes [E, K_in, N_out] and 128x128 scales [E, K_in/128,
+    N_out/128]; every 128x128 block of W^T holds the elements of one block
+    of W, so its scale is that block's scale."""
+    return (qw.transpose(1, 2).contiguous(), sw.transpose(1, 2).contiguous())
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape", [(700, 512, 384, 6, 2), (300, 1024, 256, 9, 3)])
+def test_data_gradient_through_the_transposed_weight(dev, shape, out_dtype):
+    """dX = dY W of a grouped linear layer: the contiguous grouped GEMM with
+    the transposed weight codes and scales, against the oracle's dY W."""
+    import moe_cases
+    from oracle import scaling
+    tokens, hidden, inter, experts, topk = shape
+    c = inputs.ContiguousCase(tokens=tokens, hidden=hidden, inter=inter, inter2=128,
+                              experts=experts, topk=topk, workload=34)
+    ids, _, w1, _ = inputs.contiguous_sources(c)
+    lay = moe_cases.contiguous_layout(ids, experts)
+    g = np.random.default_rng(320)
+    dy = g.standard_normal((lay.m_total, inter)).astype(np.float32)
+    dy[lay.row_token < 0] = 0.0
+    qdy, sdy = scaling.quantize_1x128(dy)
+    qw, sw = scaling.quantize_128x128(w1)
+    C, S, F = _dx_reference(qdy, sdy, qw, sw, lay.block_expert)
+    print(f"data gradient {shape} out={out_dtype}", flush=True)
+    tq, ts = _transposed_weight(torch.from_numpy(qw).cuda(), torch.from_numpy(sw).cuda())
+    d = fg8.grouped_gemm_fp8_contiguous(torch.from_numpy(qdy).cuda(), torch.from_numpy(sdy).cuda(),
+                                        tq, ts, torch.from_numpy(lay.block_expert).cuda(),
+                                        out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    if out_dtype == torch.float32:
+        check_f32(d.cpu().numpy(), C, S, inter, "dX", S_flush=F)
+    else:
+        check_bf16(d.view(torch.int16).cpu().numpy().view(np.uint16), C, S, inter, "dX",
+                   S_flush=F)
+
+
+def test_data_gradient_full_size_sampled(dev):
+    """dX = dG W1 at the MoE size (8192 tokens, top-8 of 32 experts; dG
+    [rows, 4096], W1 [32, 4096, 7168]): the GPU quantizes dG and W1 and
+    transposes W1's codes and scales; the oracle quantizes sampled rows of
+    every expert and two 128-column blocks of dX's columns itself."""
+    import moe_cases
+    from oracle import scaling
+    c = inputs.ContiguousCase()
+    ids, _, w1, _ = inputs.contiguous_sources(c)
+    lay = moe_cases.contiguous_layout(ids, c.experts)
+    g = np.random.default_rng(321)
+    dy = g.standard_normal((lay.m_total, c.inter)).astype(np.float32)
+    dy[lay.row_token < 0] = 0.0
+    tq, ts = fg8.fp8_quantize(torch.from_numpy(w1).cuda(), "128x128")
+    tq, ts = _transposed_weight(tq, ts)
+    qdy, sdy = fg8.fp8_quantize(torch.from_numpy(dy).cuda(), "1x128")
+    d = fg8.grouped_gemm_fp8_contiguous(qdy, sdy, tq, ts,
+                                        torch.from_numpy(lay.block_expert).cuda(),
+                                        out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    out = d.view(torch.int16).cpu().numpy().view(np.uint16)
+    del tq, ts, qdy, sdy, d
+    cbs = g.choice(c.hidden // 128, 2, replace=False)
+    cols = np.concatenate([np.arange(cb * 128, cb * 128 + 128) for cb in cbs])
+    rows_e = np.repeat(lay.block_expert, 128)
+    for e in range(c.experts):
+        own = np.nonzero(rows_e == e)[0]
+        if own.size == 0:
+            continue
+        rows = np.unique(np.concatenate([own[:4], own[-1:], g.choice(own, 8)]))
+        qdy_o, sdy_o = scaling.quantize_1x128(dy[rows])
+        W = np.concatenate([scaling.quantize_128x128(w1[e][:, cb * 128:(cb + 1) * 128])[0]
+                            for cb in cbs], axis=1)
+        sW = np.concatenate([scaling.quantize_128x128(w1[e][:, cb * 128:(cb + 1) * 128])[1]
+                             for cb in cbs], axis=1)
+        C, S = _dx_rows(qdy_o, sdy_o, W, sW)
+        F = ref_blockscaled(qdy_o, sdy_o, W.T.copy(), sW.T.copy())[2]
+        check_bf16(out[np.ix_(rows, cols)], C, S, c.inter, f"dX expert {e}", S_flush=F)

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import moe_grouped_gemm_fp8_amd as fg8
-from moe_grouped_gemm_fp8_amd import inputs
+import inputs
 from oracle import e4m3, gemm, scaling
 from parity import check_bf16, check_f32, ref_blockscaled
 

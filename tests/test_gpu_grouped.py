@@ -5,9 +5,10 @@ import pytest
 import torch
 
 import moe_grouped_gemm_fp8_amd as fg8
-from moe_grouped_gemm_fp8_amd import inputs
+import inputs
+import moe_cases
 from oracle import e4m3, gemm, scaling
-from parity import check_bf16, check_f32, ref_blockscaled, ref_mx
+from parity import TruncRows, check_bf16, check_f32, ref_blockscaled, ref_mx
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +35,7 @@ def _check(d, C, S, K, where, derived=True, F=0.0):
 def _small_contiguous(tokens=300, hidden=512, inter=384, experts=6, topk=2):
     c = inputs.ContiguousCase(tokens=tokens, hidden=hidden, inter=inter, inter2=256,
                               experts=experts, topk=topk, workload=31)
-    return c, inputs.contiguous_case(c)
+    return c, moe_cases.contiguous_case(c)
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
@@ -47,7 +48,7 @@ def test_contiguous_small(dev, shape, out_dtype):
     ta, tsa, tb, tsb, tbe = _gpu(qa, sa, qb, sb, lay.block_expert)
     d = fg8.grouped_gemm_fp8_contiguous(ta, tsa, tb, tsb, tbe, out_dtype=out_dtype)
     torch.cuda.synchronize()
-    F = np.zeros_like(C)
+    F = TruncRows(C.shape)
     for e in range(c.experts):
         rows = np.repeat(lay.block_expert == e, 128)
         if rows.any():
@@ -59,10 +60,10 @@ def test_contiguous_zero_expert_and_padding(dev):
     """Experts with no rows have no blocks; padding rows of A are zero and come
     out as exact zeros."""
     routing = np.array([[0, 2], [2, 3], [0, 3]] * 50, np.int32)     # expert 1 unused
-    lay = inputs.contiguous_layout(routing, 5)                       # expert 4 unused too
+    lay = moe_cases.contiguous_layout(routing, 5)                       # expert 4 unused too
     assert lay.counts[1] == 0 and lay.counts[4] == 0
     x = inputs._normal(inputs.rng(32, 0), (routing.shape[0], 256))
-    a = inputs.gather_rows(x, lay.row_token)
+    a = moe_cases.gather_rows(x, lay.row_token)
     w = inputs._normal(inputs.rng(32, 1), (5, 160, 256), 256 ** -0.5)
     qa, sa = scaling.quantize_1x128(a)
     qb, sb = scaling.quantize_128x128(w)
@@ -96,7 +97,7 @@ def test_contiguous_out_of_range_expert_ids_skip_their_block(dev):
     rows_bad = np.repeat(bad, 128)
     assert np.all(d[rows_bad] == SENTINEL_F32)
     good = ~rows_bad
-    F = np.zeros_like(C)
+    F = TruncRows(C.shape)
     for e in range(c.experts):
         rows = np.repeat((lay.block_expert == e) & ~bad, 128)
         if rows.any():
@@ -111,7 +112,7 @@ def test_contiguous_full_size_sampled(dev, which):
     multiplies everything; the oracle checks sampled rows of every expert
     against two 128-column blocks, quantized by itself from the FP32 sources."""
     c = inputs.ContiguousCase()
-    lay, a1, w1, a2, w2 = inputs.contiguous_case(c)
+    lay, a1, w1, a2, w2 = moe_cases.contiguous_case(c)
     A, W = (a1, w1) if which == "w1" else (a2, w2)
     del a1, w1, a2, w2
     K = A.shape[1]
@@ -152,7 +153,7 @@ def test_contiguous_mx_small(dev, shape, out_dtype):
     ta, tea, tb, teb, tbe = _gpu(qa, ea, qb, eb, lay.block_expert)
     d = fg8.grouped_gemm_mxfp8_contiguous(ta, tea, tb, teb, tbe, out_dtype=out_dtype)
     torch.cuda.synchronize()
-    F = np.zeros_like(C)
+    F = TruncRows(C.shape)
     for e in range(c.experts):
         rows = np.repeat(lay.block_expert == e, 128)
         if rows.any():
@@ -184,7 +185,7 @@ def test_contiguous_mx_bf16_sources_full_size_sampled(dev):
     The oracle quantizes the same BF16 values (widened) itself and checks
     sampled rows of every expert against two 128-column blocks."""
     c = inputs.ContiguousCase()
-    lay, a1, w1, a2, w2 = inputs.contiguous_case(c)
+    lay, a1, w1, a2, w2 = moe_cases.contiguous_case(c)
     del a2, w2
     tA = torch.from_numpy(a1).cuda().bfloat16()
     tW = torch.from_numpy(w1).cuda().bfloat16()

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 import moe_grouped_gemm_fp8_amd as fg8
-from moe_grouped_gemm_fp8_amd import inputs
+import inputs
 from oracle import e4m3, scaling
 
 pytestmark = pytest.mark.gpu

@@ -7,7 +7,8 @@ import pytest
 import torch
 
 import moe_grouped_gemm_fp8_amd as fg8
-from moe_grouped_gemm_fp8_amd import inputs
+import inputs
+import moe_cases
 from oracle import scaling
 from parity import check_swiglu_quant, ref_blockscaled
 
@@ -21,7 +22,7 @@ def _gpu(*arrays):
 def _case(tokens, hidden, inter, experts, topk, workload=33):
     c = inputs.ContiguousCase(tokens=tokens, hidden=hidden, inter=inter, inter2=256,
                               experts=experts, topk=topk, workload=workload)
-    lay, a1, w1, _, _ = inputs.contiguous_case(c)
+    lay, a1, w1, _, _ = moe_cases.contiguous_case(c)
     return c, lay, a1, w1
 
 
@@ -74,16 +75,19 @@ def test_swiglu_skips_out_of_range_blocks(dev):
             check_swiglu_quant(q[rows], s[:, rows], C, S, F, c.hidden, f"expert {e}")
 
 
-def test_swiglu_full_size_sampled(dev):
+def test_swiglu_full_size_every_row(dev):
     """8192 tokens, top-8 of 32 experts (Zipf 1.1), W1 7168 -> 4096 with the
     activation fused: the GPU quantizes and multiplies everything; the oracle
-    quantizes sampled rows and two gate/up block pairs itself and checks the
-    two 128-column blocks of h they give."""
+    quantizes the token rows and two gate/up block pairs of every expert
+    itself and checks the two 128-column blocks of h they give on every
+    routed row of every expert (padding rows: codes 0, scale 1)."""
     c = inputs.ContiguousCase()
-    lay, a1, w1, a2, w2 = inputs.contiguous_case(c)
-    del a2, w2
+    ids, x, w1, _ = inputs.contiguous_sources(c)
+    lay = moe_cases.contiguous_layout(ids, c.experts)
+    a1 = moe_cases.gather_rows(x, lay.row_token)
     K = a1.shape[1]
     tA, tW = _gpu(a1, w1)
+    del a1
     qa, sa = fg8.fp8_quantize(tA, "1x128")
     qb, sb = fg8.fp8_quantize(tW, "128x128")
     del tA, tW
@@ -91,19 +95,29 @@ def test_swiglu_full_size_sampled(dev):
     q, s = fg8.grouped_gemm_fp8_contiguous_swiglu(qa, sa, qb, sb, tbe)
     torch.cuda.synchronize()
     q, s = q.cpu().numpy(), s.cpu().numpy()
+    del qa, sa, qb, sb
+    pad = lay.row_token < 0
+    assert np.all(q[pad] == 0) and np.all(s[:, pad] == 1.0)
+    qx, sx = scaling.quantize_1x128(x)            # token rows; a layout row holds one
+    del x
     g = np.random.default_rng(405)
     N = w1.shape[1]
-    hbs = g.choice(N // 256, 2, replace=False)
+    hbs = np.sort(g.choice(N // 256, 2, replace=False))
     hcols = np.concatenate([np.arange(j * 128, j * 128 + 128) for j in hbs])
-    for e in g.choice(c.experts, 8, replace=False):
-        blocks = np.nonzero(lay.block_expert == e)[0]
-        own = np.concatenate([np.arange(b * 128, b * 128 + 128) for b in blocks])
-        rows = np.unique(np.concatenate([own[:2], own[-1:], g.choice(own, 2)]))
-        qa_o, sa_o = scaling.quantize_1x128(a1[rows])
+    rows_e = np.repeat(lay.block_expert, 128)
+    moved = total = 0
+    for e in range(c.experts):
+        rows = np.nonzero((rows_e == e) & ~pad)[0]
+        if rows.size == 0:
+            continue
+        tok = lay.row_token[rows]
         Bq = [scaling.quantize_128x128(w1[e, j * 256 + h * 128:j * 256 + h * 128 + 128])
               for j in hbs for h in (0, 1)]
-        qb_o = np.concatenate([x for x, _ in Bq])
-        sb_o = np.concatenate([y for _, y in Bq])
-        C, S, F = ref_blockscaled(qa_o, sa_o, qb_o, sb_o)
-        check_swiglu_quant(q[np.ix_(rows, hcols)], s[np.ix_(hbs, rows)], C, S, F, K,
-                           f"expert {e}")
+        qb_o = np.concatenate([y for y, _ in Bq])
+        sb_o = np.concatenate([z for _, z in Bq])
+        C, S, F = ref_blockscaled(qx[tok], sx[:, tok], qb_o, sb_o)
+        moved += check_swiglu_quant(q[np.ix_(rows, hcols)], s[np.ix_(hbs, rows)], C, S, F, K,
+                                    f"expert {e}")
+        total += rows.size * hcols.size
+    print(f"gated epilogue, every routed row: {moved} of {total} codes off the oracle's own "
+          f"rounding of h", flush=True)

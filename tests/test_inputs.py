@@ -2,7 +2,8 @@
 asks for (row modifiers, routing without replacement, padded layout)."""
 import numpy as np
 
-from moe_grouped_gemm_fp8_amd import inputs
+import inputs
+import moe_cases
 
 
 def test_dense_cases_deterministic_and_shaped():
@@ -29,7 +30,7 @@ def test_routing_distinct_and_skewed():
 
 def test_contiguous_layout_padding_and_order():
     r = inputs.zipf_topk_routing(3, 1000, 8, 2)
-    lay = inputs.contiguous_layout(r, 8)
+    lay = moe_cases.contiguous_layout(r, 8)
     assert lay.m_total % 128 == 0
     assert lay.block_expert.shape == (lay.m_total // 128,)
     assert np.all(np.diff(lay.block_expert) >= 0)
@@ -42,8 +43,21 @@ def test_contiguous_layout_padding_and_order():
         assert np.all(np.diff(live) > 0)              # ascending token order
         assert np.all(toks[live.size:] == -1)         # padding at the end
     x = np.arange(1000 * 128, dtype=np.float32).reshape(1000, 128)
-    a = inputs.gather_rows(x, lay.row_token)
+    a = moe_cases.gather_rows(x, lay.row_token)
     assert np.all(a[lay.row_token < 0] == 0)
+    live = lay.row_token >= 0
+    assert np.array_equal(a[live], x[lay.row_token[live]])
+
+
+def test_contiguous_sources_shapes_and_determinism():
+    c = inputs.ContiguousCase(tokens=300, hidden=256, inter=384, inter2=128, experts=5, topk=2,
+                              workload=31)
+    ids, x, w1, w2 = inputs.contiguous_sources(c)
+    ids2, x2, _, _ = inputs.contiguous_sources(c)
+    assert ids.shape == (300, 2) and x.shape == (300, 256)
+    assert w1.shape == (5, 384, 256) and w2.shape == (5, 256, 128)
+    assert np.array_equal(ids, ids2) and np.array_equal(x, x2)
+    assert inputs.contiguous_a2(c, 640).shape == (640, 128)
 
 
 def test_masked_case_counts_and_junk():

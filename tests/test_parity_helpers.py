@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 from oracle import e4m3
-from parity import check_f32, trunc_bound
+from parity import Trunc, TruncRows, check_bf16, check_f32, trunc_bound, trunc_pairs
 
 
 def _codes(rows):
@@ -43,17 +43,81 @@ def test_trunc_bound_scales_per_group():
     assert four[0, 0] == 4 * one[0, 0] > 0
 
 
-def test_check_f32_skips_derived_bar_where_not_sampled():
+def test_check_f32_holds_every_output_to_the_derived_bar():
     C = np.array([[1.0, 1.0]]); S = np.array([[1.0, 1.0]])
     g = np.array([[1.0 + 5e-4, 1.0]])        # inside the stated bar, outside eps_acc
-    F = np.array([[np.nan, 0.0]])
-    check_f32(g, C, S, 128, "nan F", S_flush=F)
-    try:
-        check_f32(g, C, S, 128, "zero F", S_flush=np.zeros((1, 2)))
-    except AssertionError:
-        pass
-    else:
-        raise AssertionError("derived bar not applied")
+    check_f32(g, C, S, 128, "stated only", derived=False)
+    with pytest.raises(AssertionError):
+        check_f32(g, C, S, 128, "zero S_trunc", S_flush=np.zeros((1, 2)))
+    check_f32(g, C, S, 128, "S_trunc covers it", S_flush=np.array([[1e-3, 0.0]]))
+
+
+def test_trunc_is_evaluated_only_where_eps_acc_is_exceeded():
+    """The lazy S_trunc term is asked for the outputs above eps_acc * S and
+    for nothing else."""
+    asked = []
+
+    def fn(idx):
+        asked.append(np.array(idx))
+        return np.full(len(idx), 1.0)
+
+    C = np.zeros((3, 4)); S = np.ones((3, 4))
+    g = C.copy(); g[1, 2] = 1e-4; g[2, 0] = -2e-4
+    check_f32(g, C, S, 128, "lazy", S_flush=Trunc((3, 4), fn))
+    assert len(asked) == 1 and sorted(asked[0].tolist()) == [6, 8]
+
+
+def test_trunc_rows_and_indexing_map_to_the_right_parts():
+    t0 = Trunc((2, 3), lambda idx: 100.0 + idx)
+    t1 = Trunc((1, 3), lambda idx: 200.0 + idx)
+    R = TruncRows((4, 3))
+    R[np.array([True, False, True, False])] = t0
+    R[np.array([3])] = t1
+    assert R.at(np.arange(12)).tolist() == [100, 101, 102, 0, 0, 0, 103, 104, 105,
+                                            200, 201, 202]
+    sub = R[np.array([2, 3])]
+    assert sub.shape == (2, 3) and sub.at([0, 4]).tolist() == [103, 201]
+    assert R[1:3, 1].at([0, 1]).tolist() == [0, 104]
+
+
+def test_trunc_pairs_match_the_full_bound():
+    g = np.random.default_rng(5)
+    a = g.integers(0, 0x7E, size=(5, 256)).astype(np.uint8)
+    b = g.integers(0, 0x7E, size=(7, 256)).astype(np.uint8)
+    sc = lambda m, n, gi: np.ones(np.broadcast(m, n, gi).shape)
+    full = trunc_bound(a, b, sc)
+    ms, ns = np.array([0, 4, 2]), np.array([6, 0, 3])
+    assert np.array_equal(trunc_pairs(a, b, sc, ms, ns), full[ms, ns])
+
+
+def test_bf16_ulp_distance_counts_bf16_steps():
+    from parity import bf16_ulp_distance
+    f = lambda bits: (np.array(bits, np.uint32) << 16).view(np.float32)
+    assert bf16_ulp_distance(f([0x3F80]), f([0x3F80]))[0] == 0
+    assert bf16_ulp_distance(f([0x3F80]), f([0x3F81]))[0] == 1       # next BF16 value
+    assert bf16_ulp_distance(f([0x3F7F]), f([0x3F80]))[0] == 1       # across a binade
+    assert bf16_ulp_distance(f([0x0000]), f([0x8000]))[0] == 0       # +0 == -0
+    assert bf16_ulp_distance(f([0x0001]), f([0x8001]))[0] == 2       # across zero
+    # one BF16 step off passes the primary rule on its own
+    assert check_bf16(np.array([[0x3F81]], np.uint16), np.ones((1, 1)), np.ones((1, 1)), 128,
+                      "1 ulp") == 0
+
+
+def test_check_bf16_second_rule_and_its_count_limit():
+    """Two ulps off passes only within ulp + eps_acc*S + S_trunc, and only
+    for a handful of outputs."""
+    from parity import FALLBACK_FRACTION  # noqa: F401
+    C = np.full((1, 4), 1.0); S = np.full((1, 4), 1.0)
+    bits = np.full((1, 4), 0x3F80, np.uint16)          # 1.0 exactly
+    assert check_bf16(bits, C, S, 128, "exact") == 0
+    off2 = bits.copy(); off2[0, 0] = 0x3F82               # 2 ulps above 1.0
+    with pytest.raises(AssertionError):
+        check_bf16(off2, C, S, 128, "2 ulp, no slack")
+    assert check_bf16(off2, C, S, 128, "2 ulp, S_trunc", S_flush=np.full((1, 4), 0.01)) == 1
+    many = np.full((1, 2000), 0x3F82, np.uint16)
+    with pytest.raises(AssertionError):
+        check_bf16(many, np.ones((1, 2000)), np.ones((1, 2000)), 128, "too many",
+                   S_flush=np.full((1, 2000), 0.01))
 
 
 def test_swiglu_bounds_accept_the_oracle_and_reject_planted_mistakes():
