@@ -11,30 +11,50 @@ them; that quantization is measured on its own among the extras.  Inputs are
 resident in HBM; every step uses a different copy of A, B and D so that the
 256 MB last-level cache cannot serve them (rotation past 576 MB).
 
-The JSON line also carries the roofline of the dominant kernel (the
-64 x 2112 x 7168 GEMM, HBM-bound) timed per launch with HIP events on the
-stream it runs on, the CPU oracle timed on a bounded sample of the same step,
-and per-workload figures (prefill GEMMs, MoE contiguous W1/W2, masked, MXFP8
-masked, quantize kernels) under "extra".
+Timing: W warmup steps and exactly K timed steps, each run as one captured
+HIP graph that walks the rotation copies in order (so the figure does not
+depend on K against the number of copies); the timed graph is replayed once
+untimed first so that its upload is not timed.  The reported time per step
+is the GPU time of the K steps, between HIP events recorded on the stream
+around a replay of the K-step graph with a synchronization on both sides;
+the host wall time around a replay is reported beside it (it adds the
+latency of launching the graph, ~30 us, which weighs on short runs).  The JSON line also carries
+the cold first step, the p50 / p95 of single steps, the roofline of every
+kernel of the step (the dominant one under "roofline") timed per launch with
+HIP events on the stream it runs on, the GPU, its observed shader clock and
+the ROCm version, the CPU oracle timed on a bounded sample of the same step,
+and per-workload figures under "extra" (prefill GEMMs, MoE contiguous,
+masked and MXFP8 layouts, the routing step, the gated W1 epilogue, an
+end-to-end MoE layer chain, the backward pieces and the quantize kernels).
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+sys.path.insert(1, os.path.join(ROOT, "tests"))     # the seeded input generators
 
 PEAK_FP8_TFLOPS = 5033.0          # 256 CU x 8192 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 576 << 20          # 2 x (256 MB MALL + 8 x 4 MB L2)
 METRIC = "FP8 TFLOPS & % of FP8 MFMA peak: dense 64×2112×7168 and MoE grouped GEMM"
+CSRC = os.path.join(ROOT, "moe_grouped_gemm_fp8_amd", "csrc")
+
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summaries of the step's GEMMs; each
+# records the sha256 of the kernel source it was taken on
+TRAFFIC_FILES = {
+    "gemm 64x2112x7168": os.path.join(ROOT, "profiles", "gemm_skinny_64x2112x7168_traffic.md"),
+    "gemm 64x24576x1536": os.path.join(ROOT, "profiles", "gemm_skinny_64x24576x1536_traffic.md"),
+}
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
@@ -42,7 +62,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="comma list of extra names to run (profiling)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def log(msg):
@@ -54,22 +74,27 @@ def gemm_bytes(M, N, K, out_bytes=2):
     return M * K + N * K + 4 * kb * M + 4 * (-(-N // 128)) * kb + out_bytes * M * N
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_skinny_64x2112x7168_traffic.md")
-GEMM_SOURCE = os.path.join(ROOT, "moe_grouped_gemm_fp8_amd", "csrc", "gemm.hip")
+def quant_bytes(rows, cols):
+    """1x128 quantize of FP32 rows: 4 B read, 1 B code and 4/128 B scale written."""
+    return rows * cols * 5 + 4 * rows * (cols // 128)
 
 
-def measured_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, scaled by the copy-kernel
-    calibration recorded there; None when that summary was taken on a
-    different gemm.hip than the one built here."""
+def measured_traffic(path):
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, scaled by the copy-kernel calibration recorded there; None when
+    the summary is missing or was taken on a different kernel source than the
+    one built here."""
     import hashlib
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(path).read()
     except OSError:
         return None
     fields = dict(line.split(":", 1) for line in text.splitlines() if ":" in line)
-    digest = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    src = os.path.join(CSRC, fields.get("source_file", "gemm.hip").strip())
+    try:
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
     if fields.get("source_sha256", "").strip() != digest:
         return None
     try:
@@ -82,94 +107,156 @@ def rotations(nbytes):
     return max(1, -(-ROTATE_BYTES // max(1, nbytes)))
 
 
-def main():
-    args = parse()
+def percentile(sorted_vals, q):
+    return sorted_vals[min(len(sorted_vals) - 1, int(round(q * (len(sorted_vals) - 1))))]
+
+
+def environment(torch):
+    """GPU, ROCm and host facts for the JSON line."""
+    p = torch.cuda.get_device_properties(0)
+    env = {"gpu": torch.cuda.get_device_name(0), "arch": getattr(p, "gcnArchName", ""),
+           "cus": p.multi_processor_count, "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None)}
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        env["rocm"] = None
+    try:
+        model = [ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo")
+                 if ln.startswith("model name")]
+        env["host_cpu"] = model[0] if model else None
+    except OSError:
+        env["host_cpu"] = None
+    return env
+
+
+def read_sclk_mhz():
+    """Current shader clock of GPU 0 from rocm-smi (None if unavailable)."""
+    try:
+        r = subprocess.run(["rocm-smi", "-d", "0", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        data = json.loads(r.stdout)
+    except Exception:
+        return None
+    for card in data.values():
+        if not isinstance(card, dict):
+            continue
+        for key, val in card.items():
+            if "sclk" in key.lower():
+                digits = "".join(ch for ch in str(val) if ch.isdigit() or ch == ".")
+                try:
+                    return float(digits)
+                except ValueError:
+                    return None
+    return None
+
+
+class Timer:
+    """Graph capture and timing on one stream."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def capture(self, fns):
+        """One graph that runs the callables in order (after an eager pass)."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for f in fns:        # eager pass first: allocations, workspaces
+                f()
+        self.stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        return g
+
+    def steps(self, step_fns, steps, warmup):
+        """Time per step of exactly `steps` steps after `warmup` steps; step i
+        runs step_fns[i % len(step_fns)].  Each phase is one graph.  Returns
+        (wall, gpu, graph): wall is the host clock between two
+        synchronizations around one replay of the timed graph; gpu is the
+        time between HIP events recorded on the stream right before and
+        after another replay (the steps' own duration, without the host's
+        latency to launch the graph)."""
+        torch = self.torch
+        R = len(step_fns)
+        timed = self.capture([step_fns[(warmup + i) % R] for i in range(steps)])
+        warm = self.capture([step_fns[i % R] for i in range(warmup)]) if warmup else None
+        timed.replay()                        # upload, untimed
+        if warm is not None:
+            warm.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        timed.replay()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            e0.record(self.stream)
+            timed.replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return wall, e0.elapsed_time(e1) * 1e-3 / steps, timed
+
+    def per_launch(self, fns, n):
+        """Average duration of one launch in steady state: HIP events on the
+        launch stream around replays of a graph that runs every callable
+        back to back, divided by the launches it holds."""
+        torch = self.torch
+        g = self.capture(fns)
+        reps = max(1, -(-n // len(fns)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            g.replay()
+            e0.record(self.stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(fns))
+
+    def singles(self, fns, n):
+        """Durations (ms) of n single launches, each its own graph bracketed
+        by HIP events; sorted."""
+        torch = self.torch
+        gs = [self.capture([f]) for f in fns]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        with torch.cuda.stream(self.stream):
+            for g in gs:
+                g.replay()
+            for i, (e0, e1) in enumerate(evs):
+                e0.record(self.stream)
+                gs[i % len(gs)].replay()
+                e1.record(self.stream)
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the kernels "
               "run on one GPU's share of the work, and sharding N (dense) or the experts "
               "(grouped) across GPUs is not part of this library", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
 
     import numpy as np
     import torch
 
+    import inputs
     import moe_grouped_gemm_fp8_amd as fg8
-    from moe_grouped_gemm_fp8_amd import inputs
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     fg8._lib.lib()        # fail loudly if the HIP library is missing
     stream = torch.cuda.Stream()
-
-    def graphs_for(fns):
-        """Capture the callables (one step each, on successive rotation copies)
-        as one graph per step plus one graph running all of them in order."""
-        with torch.cuda.stream(stream):
-            for f in fns:        # eager pass first: allocations, workspaces
-                f()
-        stream.synchronize()
-        singles = []
-        for f in fns:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                f()
-            singles.append(g)
-        whole = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(whole, stream=stream):
-            for f in fns:
-                f()
-        torch.cuda.synchronize()
-        return singles, whole
-
-    def time_graphs(gs, steps, warmup):
-        """Wall time per step of exactly `steps` steps (after `warmup`)."""
-        singles, whole = gs
-        R = len(singles)
-
-        def run(n):
-            for _ in range(n // R):
-                whole.replay()
-            for j in range(n % R):
-                singles[j].replay()
-
-        run(warmup)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        run(steps)
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) / steps
-
-    def time_graph_launches(gs, n):
-        """Average duration of one launch in steady state: HIP events on the
-        launch stream around replays of the graph that runs every rotation
-        copy back to back, divided by the launches it holds."""
-        singles, whole = gs
-        R = len(singles)
-        reps = max(1, -(-n // R))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            whole.replay()
-            e0.record(stream)
-            for _ in range(reps):
-                whole.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / (reps * R)
-
-    def time_launches(fns, n):
-        """Average duration of single launches, HIP events on the launch stream."""
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(n)]
-        with torch.cuda.stream(stream):
-            for i in range(8):
-                fns[i % len(fns)]()
-            for i, (e0, e1) in enumerate(evs):
-                e0.record(stream)
-                fns[i % len(fns)]()
-                e1.record(stream)
-        torch.cuda.synchronize()
-        ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-        return sum(ms) / len(ms), ms[len(ms) // 2], ms[int(len(ms) * 0.95)]
+    timer = Timer(torch, stream)
+    env = environment(torch)
 
     # ------------------------------------------------------------ headline step
     shapes = [inputs.DENSE_CASES["skinny_a"], inputs.DENSE_CASES["skinny_b"]]
@@ -192,49 +279,87 @@ def main():
     R = max(len(cp) for _, cp in sets)
     flops_step = sum(2 * c.M * c.N * c.K for c, _ in sets)
 
-    def step_fn(r):
-        def f():
-            for c, cp in sets:
-                x = cp[r % len(cp)]
-                fg8.fp8_quantize(x["A"], "1x128", q=x["qa"], scales=x["sa"])
-                fg8.gemm_fp8_blockscaled(x["qa"], x["sa"], x["qb"], x["sb"], out=x["d"])
-        return f
+    def quant_fn(cp, r):
+        x = cp[r % len(cp)]
+        return lambda: fg8.fp8_quantize(x["A"], "1x128", q=x["qa"], scales=x["sa"])
 
-    gs = graphs_for([step_fn(r) for r in range(R)])
-    t_step = time_graphs(gs, args.steps, args.warmup)
-    value = flops_step / t_step / 1e12
-    log(f"headline step {t_step * 1e6:.2f} us, {value:.1f} TFLOP/s ({R} rotation copies)")
-
-    # dominant kernel: the 64 x 2112 x 7168 GEMM, per-launch events
-    c0, cp0 = sets[0]
-
-    def gemm_launch(r):
-        x = cp0[r % len(cp0)]
+    def gemm_fn(cp, r):
+        x = cp[r % len(cp)]
         return lambda: fg8.gemm_fp8_blockscaled(x["qa"], x["sa"], x["qb"], x["sb"], out=x["d"])
 
-    fns0 = [gemm_launch(r) for r in range(len(cp0))]
-    avg_ms = time_graph_launches(graphs_for(fns0), 400)
-    ev_avg, ev_med, ev_p95 = time_launches(fns0, 200)
-    algo = gemm_bytes(c0.M, c0.N, c0.K)
-    achieved = algo / (avg_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": measured_traffic(),
-                "kernel": "fg8::gemm_kernel, 64x32 tiles, two workgroups per CU, 2 K blocks "
-                          "per stage, 7-way split-K (64x2112x7168, BF16 out)",
-                "algorithmic_bytes": algo, "avg_us": round(avg_ms * 1e3, 3),
-                "timing": "HIP events around back-to-back graph launches on the kernel's stream",
-                "single_launch_us": {"avg": round(ev_avg * 1e3, 3), "median": round(ev_med * 1e3, 3),
-                                     "p95": round(ev_p95 * 1e3, 3)},
-                "tflops": round(2 * c0.M * c0.N * c0.K / (avg_ms * 1e-3) / 1e12, 1)}
+    def step_fn(r):
+        parts = [f(cp, r) for _, cp in sets for f in (quant_fn, gemm_fn)]
+
+        def f():
+            for p in parts:
+                p()
+        return f
+
+    step_fns = [step_fn(r) for r in range(R)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        step_fns[0]()
+    torch.cuda.synchronize()
+    cold_us = (time.perf_counter() - t0) * 1e6
+
+    t_wall, t_step, timed_graph = timer.steps(step_fns, args.steps, args.warmup)
+    value = flops_step / t_step / 1e12
+    log(f"headline step {t_step * 1e6:.2f} us (events), {t_wall * 1e6:.2f} us wall, "
+        f"{value:.1f} TFLOP/s ({R} rotation copies, cold first step {cold_us:.0f} us)")
+    single = timer.singles(step_fns, 200)
+    # the shader clock while the timed graph runs (enqueued several times)
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, 80000 // args.steps)):
+            timed_graph.replay()
+    sclk = read_sclk_mhz()
+    torch.cuda.synchronize()
+    env["sclk_mhz_under_load"] = sclk
+    del timed_graph
+
+    # every kernel of the step on its own: per-launch events over back-to-back
+    # launches of all rotation copies
+    kernels = []
+    for c, cp in sets:
+        for kind, mk in (("quantize 1x128", quant_fn), ("gemm", gemm_fn)):
+            name = f"{kind} {c.M}x{c.K}" if kind != "gemm" else f"gemm {c.M}x{c.N}x{c.K}"
+            fns = [mk(cp, r) for r in range(len(cp))]
+            avg_ms = timer.per_launch(fns, 400)
+            sl = timer.singles(fns, 100)
+            if kind == "gemm":
+                algo = gemm_bytes(c.M, c.N, c.K)
+                t = fg8.tile_choice(0, c.M, c.N, c.K)
+                desc = (f"fg8 GEMM, {t['bm']}x{t['bn']} tiles, {t['splits']}-way split-K, "
+                        f"{t['grid']} workgroups, BF16 out")
+            else:
+                algo = quant_bytes(c.M, c.K)
+                desc = "fg8 1x128 quantize, FP32 in"
+            achieved = algo / (avg_ms * 1e-3) / 1e9
+            k = {"name": name, "bound": "hbm", "achieved": round(achieved, 1),
+                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                 "traffic": measured_traffic(TRAFFIC_FILES[name]) if name in TRAFFIC_FILES
+                 else None,
+                 "kernel": desc, "algorithmic_bytes": algo, "avg_us": round(avg_ms * 1e3, 3),
+                 "single_launch_us": {"median": round(percentile(sl, 0.5) * 1e3, 3),
+                                      "p95": round(percentile(sl, 0.95) * 1e3, 3)}}
+            if kind == "gemm":
+                k["tflops"] = round(2 * c.M * c.N * c.K / (avg_ms * 1e-3) / 1e12, 1)
+            kernels.append(k)
+            log(f"{name}: {k['avg_us']} us, {k['achieved']} GB/s ({k['frac']:.3f} of HBM)")
+    dominant = max(kernels, key=lambda k: k["avg_us"])
+    roofline = {key: dominant[key] for key in ("bound", "achieved", "peak", "unit", "frac",
+                                               "traffic")}
+    roofline.update({"kernel": f"{dominant['name']}: {dominant['kernel']}",
+                     "algorithmic_bytes": dominant["algorithmic_bytes"],
+                     "avg_us": dominant["avg_us"],
+                     "timing": "HIP events around back-to-back graph launches on the kernel's "
+                               "stream", "all_kernels": kernels})
 
     extra = {}
     if not args.no_extra:
-        extra = run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launches,
-                           args)
+        extra = run_extras(fg8, inputs, torch, np, dev, timer, args)
 
-    log(f"dominant kernel avg {avg_ms * 1e3:.2f} us -> {achieved:.0f} GB/s")
-    cpu = None if args.no_cpu else cpu_baseline(np, inputs, sets)
+    cpu = None if args.no_cpu else cpu_baseline(np, inputs, [c for c, _ in sets])
     if cpu:
         log(f"cpu baseline {cpu}")
 
@@ -247,30 +372,37 @@ def main():
                                "(1x128) + block-scaled FP8 GEMM (B 128x128), BF16 out",
                    "M": 64, "N": [2112, 24576], "K": [7168, 1536], "rotation_copies": R,
                    "frac_of_fp8_peak": round(value / PEAK_FP8_TFLOPS, 5)},
+        "step_timing": {"events_us": round(t_step * 1e6, 3), "wall_us": round(t_wall * 1e6, 3),
+                        "cold_first_step_us": round(cold_us, 1),
+                        "single_step_us": {"p50": round(percentile(single, 0.5) * 1e3, 3),
+                                           "p95": round(percentile(single, 0.95) * 1e3, 3)}},
+        "env": env,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,
     }
-    print(json.dumps(line))
+    print(json.dumps(line), flush=True)
 
 
-def run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launches, args):
+def run_extras(fg8, inputs, torch, np, dev, timer, args):
     only = set(filter(None, args.only.split(",")))
     out = {}
     gen = torch.Generator(device=dev)
 
-    def randn(shape, std=1.0, seed=0):
+    def randn(shape, std=1.0, seed=0, dtype=torch.float32):
         gen.manual_seed(seed)
         t = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
-        return t.mul_(std) if std != 1.0 else t
+        if std != 1.0:
+            t.mul_(std)
+        return t if dtype == torch.float32 else t.to(dtype)
 
     def record(name, fns, flops=None, nbytes=None, steps=None):
-        gs = graphs_for(fns)
         n = steps or 100
-        t = time_graphs(gs, n, max(5, n // 10))
-        avg, med, p95 = time_launches(fns, min(100, max(20, n)))
-        r = {"ms_graph": round(t * 1e3, 4), "ms_event_avg": round(avg, 4),
-             "ms_event_median": round(med, 4), "ms_event_p95": round(p95, 4)}
+        _, t, g = timer.steps(fns, n, max(5, n // 10))
+        del g
+        sl = timer.singles(fns, min(100, max(20, n)))
+        r = {"ms": round(t * 1e3, 4), "ms_single_p50": round(percentile(sl, 0.5), 4),
+             "ms_single_p95": round(percentile(sl, 0.95), 4)}
         # rates from the steady-state (graph) time per launch
         if flops:
             r["tflops"] = round(flops / t / 1e12, 1)
@@ -299,31 +431,39 @@ def run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launch
         record(f"{nm} {c.M}x{c.N}x{c.K}", fns, 2 * c.M * c.N * c.K, gemm_bytes(c.M, c.N, c.K))
         del cps, fns
 
-    # MoE contiguous W1 / W2 (8192 tokens, top-8 of 32 experts, Zipf 1.1)
+    cc = inputs.ContiguousCase()
+    moe_names = ("contiguous", "quantize", "chain", "mxcontig", "route", "wgrad")
+    if any(want(n) for n in moe_names):
+        ids = torch.from_numpy(inputs.zipf_topk_routing(cc.workload, cc.tokens, cc.experts,
+                                                        cc.topk)).to(dev)
+
+    def layout(x):
+        """The routing step's contiguous layout (on the GPU) of token rows x."""
+        lay = fg8.moe_contiguous_layout_fp8(x, ids, cc.experts)
+        rt = lay["row_token"].long()
+        return lay, rt, rt >= 0, int(lay["expert_counts"].sum().item())
+
+    # MoE contiguous W1 / W2 (8192 tokens, top-8 of 32 experts, Zipf 1.1) in
+    # the layout the routing step builds (m_cap rows; the blocks past the last
+    # expert's run are skipped by the GEMM)
     if want("contiguous") or want("quantize"):
-        cc = inputs.ContiguousCase()
-        routing = inputs.zipf_topk_routing(cc.workload, cc.tokens, cc.experts, cc.topk)
-        lay = inputs.contiguous_layout(routing, cc.experts)
-        rt = torch.from_numpy(lay.row_token).to(dev)
-        live = rt >= 0
-        be = torch.from_numpy(lay.block_expert).to(dev)
         x = randn((cc.tokens, cc.hidden), seed=21)
-        a1 = torch.zeros((lay.m_total, cc.hidden), dtype=torch.float32, device=dev)
-        a1[live] = x[rt[live]]
-        del x
+        lay, rt, live, valid = layout(x)
+        m_cap = rt.shape[0]
+        qa1, sa1, be = lay["q"], lay["sa"], lay["block_expert"]
         if want("quantize"):
+            a1 = torch.zeros((m_cap, cc.hidden), dtype=torch.float32, device=dev)
+            a1[live] = x[rt[live]]
             R = rotations(a1.numel() * 5)
             cp = [torch.empty_like(a1, dtype=torch.uint8) for _ in range(R)]
-            sc = [torch.empty((cc.hidden // 128, lay.m_total), dtype=torch.float32, device=dev)
+            sc = [torch.empty((cc.hidden // 128, m_cap), dtype=torch.float32, device=dev)
                   for _ in range(R)]
-            fns = [(lambda i=i: fg8.fp8_quantize(a1, "1x128", q=cp[i], scales=sc[i])) for i in range(R)]
-            record(f"quantize 1x128 {lay.m_total}x{cc.hidden}", fns,
-                   nbytes=a1.numel() * 4 + a1.numel() + 4 * a1.numel() // 128)
-            del cp, sc
-        qa1, sa1 = fg8.fp8_quantize(a1, "1x128")
-        del a1
-        w1 = randn((cc.experts, cc.inter, cc.hidden), cc.hidden ** -0.5, seed=22)
-        if want("quantize"):
+            fns = [(lambda i=i: fg8.fp8_quantize(a1, "1x128", q=cp[i], scales=sc[i]))
+                   for i in range(R)]
+            record(f"quantize 1x128 {m_cap}x{cc.hidden}", fns,
+                   nbytes=quant_bytes(m_cap, cc.hidden))
+            del cp, sc, a1
+            w1 = randn((cc.experts, cc.inter, cc.hidden), cc.hidden ** -0.5, seed=22)
             q = torch.empty_like(w1, dtype=torch.uint8)
             s = torch.empty((cc.experts, cc.inter // 128, cc.hidden // 128), dtype=torch.float32,
                             device=dev)
@@ -335,112 +475,127 @@ def run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launch
             record(f"quantize mx1x32 {cc.experts}x{cc.inter}x{cc.hidden}",
                    [lambda: fg8.fp8_quantize(w1, "mx", q=qx, scales=ex)],
                    nbytes=w1.numel() * 5 + w1.numel() // 32)
-            del q, s, qx, ex
-        if not want("contiguous"):
-            del w1, qa1, sa1
-        else:
-            qw1, sw1 = fg8.fp8_quantize(w1, "128x128")
-            del w1
-            d1 = torch.empty((lay.m_total, cc.inter), dtype=torch.bfloat16, device=dev)
-            fl = 2 * lay.valid_rows * cc.inter * cc.hidden
-            nb = (lay.m_total * cc.hidden + qw1.numel() + 4 * sa1.numel() + 4 * sw1.numel()
-                  + 2 * d1.numel())
-            record(f"moe contiguous W1 {lay.m_total}(valid {lay.valid_rows})x{cc.inter}x{cc.hidden}",
-                   [lambda: fg8.grouped_gemm_fp8_contiguous(qa1, sa1, qw1, sw1, be, out=d1)], fl, nb,
-                   steps=20)
+            del q, s, qx, ex, w1
+        del x
+        if want("contiguous"):
+            qw1, sw1 = fg8.fp8_quantize(
+                randn((cc.experts, cc.inter, cc.hidden), cc.hidden ** -0.5, seed=22), "128x128")
+            d1 = torch.empty((m_cap, cc.inter), dtype=torch.bfloat16, device=dev)
+            fl = 2 * valid * cc.inter * cc.hidden
+            nb = (valid * cc.hidden + qw1.numel() + 4 * valid * cc.hidden // 128 + 4 * sw1.numel()
+                  + 2 * valid * cc.inter)
+            record(f"moe contiguous W1 {m_cap}(valid {valid})x{cc.inter}x{cc.hidden}",
+                   [lambda: fg8.grouped_gemm_fp8_contiguous(qa1, sa1, qw1, sw1, be, out=d1)],
+                   fl, nb, steps=20)
             # the same W1 GEMM with the SiLU-gated activation and the 1x128
             # quantization of W2's input fused into the epilogue (the weight
             # rows read as interleaved gate / up blocks)
-            qh = torch.empty((lay.m_total, cc.inter // 2), dtype=torch.uint8, device=dev)
-            sh = torch.empty((cc.inter // 256, lay.m_total), dtype=torch.float32, device=dev)
-            nb = (lay.m_total * cc.hidden + qw1.numel() + 4 * sa1.numel() + 4 * sw1.numel()
-                  + qh.numel() + 4 * sh.numel())
+            qh = torch.empty((m_cap, cc.inter // 2), dtype=torch.uint8, device=dev)
+            sh = torch.empty((cc.inter // 256, m_cap), dtype=torch.float32, device=dev)
+            nb = (valid * cc.hidden + qw1.numel() + 4 * valid * cc.hidden // 128 + 4 * sw1.numel()
+                  + valid * cc.inter // 2 + 4 * valid * cc.inter // 256)
             record(f"moe contiguous W1 + SiLU-gated activation + 1x128 quantize "
-                   f"{lay.m_total}(valid {lay.valid_rows})x{cc.inter}x{cc.hidden}",
+                   f"{m_cap}(valid {valid})x{cc.inter}x{cc.hidden}",
                    [lambda: fg8.grouped_gemm_fp8_contiguous_swiglu(qa1, sa1, qw1, sw1, be,
                                                                     q_out=qh, s_out=sh)],
                    fl, nb, steps=20)
-            del qa1, sa1, qw1, sw1, d1, qh, sh
-            a2 = randn((lay.m_total, cc.inter2), seed=23)
+            del qw1, sw1, d1, qh, sh
+            a2 = randn((m_cap, cc.inter2), seed=23)
             a2[~live] = 0
             qa2, sa2 = fg8.fp8_quantize(a2, "1x128")
             del a2
-            w2 = randn((cc.experts, cc.hidden, cc.inter2), cc.inter2 ** -0.5, seed=24)
-            qw2, sw2 = fg8.fp8_quantize(w2, "128x128")
-            del w2
-            d2 = torch.empty((lay.m_total, cc.hidden), dtype=torch.bfloat16, device=dev)
-            fl = 2 * lay.valid_rows * cc.hidden * cc.inter2
-            nb = (qa2.numel() + qw2.numel() + 4 * sa2.numel() + 4 * sw2.numel() + 2 * d2.numel())
-            record(f"moe contiguous W2 {lay.m_total}(valid {lay.valid_rows})x{cc.hidden}x{cc.inter2}",
-                   [lambda: fg8.grouped_gemm_fp8_contiguous(qa2, sa2, qw2, sw2, be, out=d2)], fl, nb,
-                   steps=20)
+            qw2, sw2 = fg8.fp8_quantize(
+                randn((cc.experts, cc.hidden, cc.inter2), cc.inter2 ** -0.5, seed=24), "128x128")
+            d2 = torch.empty((m_cap, cc.hidden), dtype=torch.bfloat16, device=dev)
+            fl = 2 * valid * cc.hidden * cc.inter2
+            nb = (valid * cc.inter2 + qw2.numel() + 4 * valid * cc.inter2 // 128 + 4 * sw2.numel()
+                  + 2 * valid * cc.hidden)
+            record(f"moe contiguous W2 {m_cap}(valid {valid})x{cc.hidden}x{cc.inter2}",
+                   [lambda: fg8.grouped_gemm_fp8_contiguous(qa2, sa2, qw2, sw2, be, out=d2)],
+                   fl, nb, steps=20)
             del qa2, sa2, qw2, sw2, d2
+        del lay, qa1, sa1, be, rt, live
+
+    # One MoE expert layer end to end: routing of the BF16 token rows into
+    # the contiguous layout with their 1x128 quantization, W1 with the gated
+    # activation and the requantization of h fused, then W2 with BF16 out
+    if want("chain"):
+        xb = randn((cc.tokens, cc.hidden), seed=21, dtype=torch.bfloat16)
+        lay, rt, live, valid = layout(xb)
+        m_cap = rt.shape[0]
+        qw1, sw1 = fg8.fp8_quantize(
+            randn((cc.experts, cc.inter, cc.hidden), cc.hidden ** -0.5, seed=22), "128x128")
+        qw2, sw2 = fg8.fp8_quantize(
+            randn((cc.experts, cc.hidden, cc.inter2), cc.inter2 ** -0.5, seed=24), "128x128")
+        qh = torch.empty((m_cap, cc.inter // 2), dtype=torch.uint8, device=dev)
+        sh = torch.empty((cc.inter // 256, m_cap), dtype=torch.float32, device=dev)
+        y = torch.empty((m_cap, cc.hidden), dtype=torch.bfloat16, device=dev)
+
+        def chain():
+            fg8.moe_contiguous_layout_fp8(xb, ids, cc.experts, out=lay)
+            fg8.grouped_gemm_fp8_contiguous_swiglu(lay["q"], lay["sa"], qw1, sw1,
+                                                   lay["block_expert"], q_out=qh, s_out=sh)
+            fg8.grouped_gemm_fp8_contiguous(qh, sh, qw2, sw2, lay["block_expert"], out=y)
+        fl = 2 * valid * cc.inter * cc.hidden + 2 * valid * cc.hidden * cc.inter2
+        record(f"moe layer chain: routing + quantize (bf16 {cc.tokens}x{cc.hidden}, top{cc.topk} "
+               f"of {cc.experts}) -> W1 + gated activation + requantize -> W2 (bf16 out)",
+               [chain], fl, steps=10)
+        del xb, lay, qw1, sw1, qw2, sw2, qh, sh, y
 
     # MoE contiguous W1 with MXFP8 operands from BF16 sources (the training
     # pipeline: BF16 -> MXFP8 quantize -> grouped GEMM -> BF16)
     if want("mxcontig"):
-        cc = inputs.ContiguousCase()
-        routing = inputs.zipf_topk_routing(cc.workload, cc.tokens, cc.experts, cc.topk)
-        lay = inputs.contiguous_layout(routing, cc.experts)
-        rt = torch.from_numpy(lay.row_token).to(dev)
-        live = rt >= 0
-        be = torch.from_numpy(lay.block_expert).to(dev)
-        x = randn((cc.tokens, cc.hidden), seed=21).bfloat16()
-        a1 = torch.zeros((lay.m_total, cc.hidden), dtype=torch.bfloat16, device=dev)
-        a1[live] = x[rt[live]]
-        del x
+        xb = randn((cc.tokens, cc.hidden), seed=21, dtype=torch.bfloat16)
+        lay, rt, live, valid = layout(xb)
+        m_cap = rt.shape[0]
+        a1 = torch.zeros((m_cap, cc.hidden), dtype=torch.bfloat16, device=dev)
+        a1[live] = xb[rt[live]]
+        be = lay["block_expert"]
+        del xb, lay
         qa = torch.empty_like(a1, dtype=torch.uint8)
-        ea = torch.empty((lay.m_total, cc.hidden // 32), dtype=torch.uint8, device=dev)
-        record(f"quantize mx1x32 from bf16 {lay.m_total}x{cc.hidden}",
+        ea = torch.empty((m_cap, cc.hidden // 32), dtype=torch.uint8, device=dev)
+        record(f"quantize mx1x32 from bf16 {m_cap}x{cc.hidden}",
                [lambda: fg8.fp8_quantize(a1, "mx", q=qa, scales=ea)],
                nbytes=a1.numel() * 3 + a1.numel() // 32)
         del a1
-        w1 = randn((cc.experts, cc.inter, cc.hidden), cc.hidden ** -0.5, seed=22).bfloat16()
-        qw, ew = fg8.fp8_quantize(w1, "mx")
-        del w1
-        d1 = torch.empty((lay.m_total, cc.inter), dtype=torch.bfloat16, device=dev)
-        fl = 2 * lay.valid_rows * cc.inter * cc.hidden
-        nb = qa.numel() + ea.numel() + qw.numel() + ew.numel() + 2 * d1.numel()
-        record(f"moe contiguous mxfp8 W1 {lay.m_total}(valid {lay.valid_rows})x{cc.inter}x{cc.hidden}",
+        qw, ew = fg8.fp8_quantize(randn((cc.experts, cc.inter, cc.hidden), cc.hidden ** -0.5,
+                                        seed=22, dtype=torch.bfloat16), "mx")
+        d1 = torch.empty((m_cap, cc.inter), dtype=torch.bfloat16, device=dev)
+        fl = 2 * valid * cc.inter * cc.hidden
+        nb = valid * cc.hidden * (1 + 1 / 32) + qw.numel() + ew.numel() + 2 * valid * cc.inter
+        record(f"moe contiguous mxfp8 W1 {m_cap}(valid {valid})x{cc.inter}x{cc.hidden}",
                [lambda: fg8.grouped_gemm_mxfp8_contiguous(qa, ea, qw, ew, be, out=d1)], fl, nb,
                steps=20)
-        del qa, ea, qw, ew, d1
+        del qa, ea, qw, ew, d1, be
 
     # MoE routing -> contiguous layout + 1x128 quantize of the BF16 token rows
     # into the rows that hold them (the step before the contiguous W1 GEMM).
     # Bytes: every token row read once, the ids, and the layout's codes,
     # scales, row map and its inverse written once.
     if want("route"):
-        cc = inputs.ContiguousCase()
-        ids = torch.from_numpy(inputs.zipf_topk_routing(cc.workload, cc.tokens, cc.experts,
-                                                        cc.topk)).to(dev)
-        x = randn((cc.tokens, cc.hidden), seed=21).bfloat16()
+        xb = randn((cc.tokens, cc.hidden), seed=21, dtype=torch.bfloat16)
         cap = fg8.moe_capacity(cc.tokens, cc.topk, cc.experts)
-        lay = fg8.moe_contiguous_layout_fp8(x, ids, cc.experts)
+        lay = fg8.moe_contiguous_layout_fp8(xb, ids, cc.experts)
         valid = int(lay["expert_counts"].sum())
-        nb = (2 * x.numel() + 8 * ids.numel() + cap * cc.hidden + 4 * cap * cc.hidden // 128
+        nb = (2 * xb.numel() + 8 * ids.numel() + cap * cc.hidden + 4 * cap * cc.hidden // 128
               + 4 * cap + 4 * cap // 128 + 8 * cc.experts + 4)
         record(f"moe routing + quantize 1x128 from bf16 into the layout {cc.tokens}x{cc.hidden} "
                f"top{cc.topk} of {cc.experts} (m_cap {cap}, routed {valid})",
-               [lambda: fg8.moe_contiguous_layout_fp8(x, ids, cc.experts, out=lay)], nbytes=nb)
-        del x, ids, lay
+               [lambda: fg8.moe_contiguous_layout_fp8(xb, ids, cc.experts, out=lay)], nbytes=nb)
+        del xb, lay
 
     # Training backward of W1: dY and X quantized along the token axis
     # (transposed codes), then the K-grouped weight-gradient GEMM over the
     # routing layout's expert row ranges, FP32 dW [32][4096][7168]
     if want("wgrad"):
-        cc = inputs.ContiguousCase()
-        ids = torch.from_numpy(inputs.zipf_topk_routing(cc.workload, cc.tokens, cc.experts,
-                                                        cc.topk)).to(dev)
-        xb = randn((cc.tokens, cc.hidden), seed=21).bfloat16()
-        lay = fg8.moe_contiguous_layout_fp8(xb, ids, cc.experts)
+        xb = randn((cc.tokens, cc.hidden), seed=21, dtype=torch.bfloat16)
+        lay, rt, live, valid = layout(xb)
         offs = lay["expert_offsets"]
         M = int(offs[-1].item())
-        rt = lay["row_token"][:M].long()
-        live = rt >= 0
+        rt, live = rt[:M], live[:M]
         X = torch.zeros((M, cc.hidden), dtype=torch.bfloat16, device=dev)
         X[live] = xb[rt[live]]
-        dy = randn((M, cc.inter), seed=25).bfloat16()
+        dy = randn((M, cc.inter), seed=25, dtype=torch.bfloat16)
         dy[~live] = 0
         del xb, lay
         qx = torch.empty((cc.hidden, M), dtype=torch.uint8, device=dev)
@@ -451,7 +606,6 @@ def run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launch
         qy, sy = fg8.fp8_quantize(dy, "1x128_t")
         del X, dy
         dw = torch.empty((cc.experts, cc.inter, cc.hidden), dtype=torch.float32, device=dev)
-        valid = int(live.sum().item())
         fl = 2 * valid * cc.inter * cc.hidden
         nb = qy.numel() + qx.numel() + 4 * (sy.numel() + sx.numel()) + 4 * dw.numel()
         record(f"moe wgrad W1 k-grouped {cc.experts}x{cc.inter}x{cc.hidden} over {M} rows "
@@ -495,21 +649,27 @@ def run_extras(fg8, inputs, torch, np, dev, graphs_for, time_graphs, time_launch
     return out
 
 
-def cpu_baseline(np, inputs, sets):
+def cpu_baseline(np, inputs, shapes, budget_s=15.0):
     """The oracle, as it stands, timed on this host on a bounded sample of the
-    step: it quantizes A and runs the float64 GEMM for the 64 x 2112 x 7168
-    shape (B quantized once outside the timing, as on the GPU)."""
+    step: whole steps (quantize A 1x128 + float64 GEMM for both skinny
+    shapes; B quantized once outside the timing, as on the GPU) repeated
+    until the budget is spent."""
     from oracle import gemm, scaling
-    A, B = inputs.dense_case("skinny_a")
-    qb, sb = scaling.quantize_128x128(B)
-    flops = 2 * A.shape[0] * B.shape[0] * A.shape[1]
+    ops = []
+    flops = 0
+    for c in shapes:
+        A, B = inputs.dense_case("skinny_a" if c.N == 2112 else "skinny_b")
+        qb, sb = scaling.quantize_128x128(B)
+        ops.append((A, qb, sb))
+        flops += 2 * c.M * c.N * c.K
     n, t0 = 0, time.perf_counter()
     while True:
-        qa, sa = scaling.quantize_1x128(A)
-        gemm.gemm_blockscaled(qa, sa, qb, sb)
+        for A, qb, sb in ops:
+            qa, sa = scaling.quantize_1x128(A)
+            gemm.gemm_blockscaled(qa, sa, qb, sb)
         n += 1
         el = time.perf_counter() - t0
-        if el > 10.0 or n >= 200:
+        if el > budget_s or n >= 200:
             break
     try:
         from threadpoolctl import threadpool_info
@@ -518,8 +678,8 @@ def cpu_baseline(np, inputs, sets):
         cores = os.cpu_count()
     return {"value": round(flops * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{n} oracle steps of quantize A 1x128 + float64 GEMM 64x2112x7168 "
-                      f"({el:.1f} s)"}
+            "sample": f"{n} oracle steps of quantize A 1x128 + float64 GEMM for 64x2112x7168 and "
+                      f"64x24576x1536 ({el:.1f} s)"}
 
 
 if __name__ == "__main__":

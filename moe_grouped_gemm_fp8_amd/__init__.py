@@ -17,5 +17,6 @@ from ._lib import (  # noqa: F401
     grouped_gemm_mxfp8_contiguous,
     moe_capacity,
     moe_contiguous_layout_fp8,
+    tile_choice,
     version,
 )

@@ -121,6 +121,17 @@ def version() -> int:
     return lib().fg8_version()
 
 
+def tile_choice(mode, m, n, k, groups=1, num_cus=None):
+    """The tiling the library picks for a GEMM of this shape (fg8_tile_choice;
+    mode 0 dense, 1 contiguous, 2 masked, 3 K-grouped): dict of bm, bn,
+    splits, grid, raster.  num_cus defaults to the current device's."""
+    if num_cus is None:
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    out = (ctypes.c_int32 * 5)()
+    _check(lib().fg8_tile_choice(mode, m, n, k, groups, num_cus, ctypes.cast(out, ctypes.c_void_p)))
+    return dict(zip(("bm", "bn", "splits", "grid", "raster"), list(out)))
+
+
 # --------------------------------------------------------------- quantize
 def fp8_quantize(x, kind="1x128", q=None, scales=None):
     """x float32 or bfloat16 [..., rows, cols] -> (q uint8, scales); see fg8.h
