@@ -140,6 +140,29 @@ fg8_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t
 /* Workspace bytes gemm_fp8_blockscaled needs for this shape (0 if none). */
 size_t fg8_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
+/* Bytes of the per-GPU scratch array of gemm_fp8_blockscaled_noalloc. */
+#define FG8_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * gemm_fp8_blockscaled_noalloc: gemm_fp8_blockscaled without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, layouts, kernels and results as gemm_fp8_blockscaled.
+ *   The split-K counters and partial sums live in a static device array of
+ *   FG8_NOALLOC_SCRATCH_BYTES (16 MiB), one per GPU the library runs on,
+ *   held until the process ends; its address is looked up at the first call
+ *   on each device, which also clears its counters on `stream`.  A shape
+ *   whose fg8_gemm_workspace_bytes exceeds that size is FG8_EUNSUPPORTED
+ *   (nothing launched).  The call allocates nothing.
+ *   Every call on one GPU shares that GPU's array: calls that can overlap on
+ *   one GPU (other streams, other threads) race and must not be issued;
+ *   calls queued on one stream are fine, since each completed call leaves
+ *   the counters at zero again.
+ */
+fg8_status gemm_fp8_blockscaled_noalloc(const uint8_t* a, const float* sa, const uint8_t* b,
+                                        const float* sb, void* d, fg8_out out, int64_t m,
+                                        int64_t n, int64_t k, hipStream_t stream);
+
 /*
  * grouped_gemm_fp8_contiguous: MoE grouped GEMM, contiguous layout (DeepGEMM
  * release news, ctol-kr.com, section 4; DeepGEMM explainer, MoE section).  The

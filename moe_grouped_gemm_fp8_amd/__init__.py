@@ -8,6 +8,7 @@ from ._lib import (  # noqa: F401
     Fg8Error,
     fp8_quantize,
     gemm_fp8_blockscaled,
+    gemm_fp8_blockscaled_noalloc,
     gemm_mxfp8,
     gemm_workspace_bytes,
     grouped_gemm_fp8_contiguous,

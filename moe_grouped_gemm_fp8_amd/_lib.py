@@ -28,6 +28,8 @@ _SIGNATURES = {
     "fp8_quantize_bf16": [_c_ptr, _c_i64, _c_i64, _c_i64, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr],
     "gemm_fp8_blockscaled": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int, _c_i64, _c_i64,
                              _c_i64, _c_ptr, ctypes.c_size_t, _c_ptr],
+    "gemm_fp8_blockscaled_noalloc": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int,
+                                     _c_i64, _c_i64, _c_i64, _c_ptr],
     "grouped_gemm_fp8_contiguous": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, ctypes.c_int,
                                     _c_i64, _c_i64, _c_i64, _c_i32, _c_ptr],
     "grouped_gemm_fp8_contiguous_swiglu": [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
@@ -200,6 +202,26 @@ def gemm_fp8_blockscaled(a, sa, b, sb, out_dtype=torch.bfloat16, out=None, works
                                       _out_code(out.dtype), m, n, k, _ptr(ws),
                                       0 if ws is None else ws.numel() * ws.element_size(),
                                       _stream()))
+    return out
+
+
+def gemm_fp8_blockscaled_noalloc(a, sa, b, sb, out_dtype=torch.bfloat16, out=None):
+    """gemm_fp8_blockscaled without a workspace: the split-K scratch is the
+    library's static per-GPU array (see fg8.h).  `out` must be given by
+    callers that cannot allocate; calls that overlap on one GPU race."""
+    _fp8(a, "a"); _fp8(b, "b")
+    _dev(sa, torch.float32, "sa"); _dev(sb, torch.float32, "sb")
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k or sa.shape != (k // 128, m) or sb.shape != (-(-n // 128), k // 128):
+        raise ValueError("operand shapes disagree")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _dev(out, out.dtype, "out")
+    if out.shape != (m, n):
+        raise ValueError("output shape disagrees")
+    _check(lib().gemm_fp8_blockscaled_noalloc(_ptr(a), _ptr(sa), _ptr(b), _ptr(sb), _ptr(out),
+                                              _out_code(out.dtype), m, n, k, _stream()))
     return out
 
 

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fg8.h"
 #include "fg8_internal.h"
 
@@ -152,6 +154,100 @@ fg8_status gemm_fp8_blockscaled(const uint8_t* a, const float* sa, const uint8_t
     if (!aligned16(workspace)) return fail(FG8_EINVAL, "%s: workspace misaligned", fn);
     p.ws_counters = (int32_t*)workspace;
     p.ws_partial = (float*)((char*)workspace + fg8::kSplitKCounterBytes);
+  }
+  const hipError_t e = fg8::launch_gemm(p, t, stream);
+  if (e != hipSuccess) return fail(FG8_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  g_err[0] = 0;
+  return FG8_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free dense GEMM (gemm_fp8_blockscaled_noalloc):
+// the split-K arrival counters and partial sums live in this array, one copy
+// per GPU, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it names a stand-in, not device memory):
+// each device's address is looked up once with hipGetSymbolAddress and kept.
+static_assert(FG8_NOALLOC_SCRATCH_BYTES > fg8::kSplitKCounterBytes, "scratch holds the counters");
+static __device__ __align__(256) uint8_t scratch[FG8_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Zeroes n 32-bit words (the arrival counters) without hipMemsetAsync, so
+// that the first call on a device may be captured into a graph.
+__global__ void zero_words(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// The device address of this device's scratch, looked up (and its counters
+// cleared, on the caller's stream) at the first call on the device.
+fg8_status scratch_ptr(const char* fn, hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(FG8_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(FG8_EUNSUPPORTED, "%s: device %d", fn, dev);
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&] {
+    void* p = nullptr;
+    s.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (s.err == hipSuccess) {
+      hipLaunchKernelGGL(zero_words, dim3(1), dim3(256), 0, stream, (uint32_t*)p,
+                         (int)(fg8::kSplitKCounterBytes / 4));
+      s.err = hipGetLastError();
+    }
+    if (s.err == hipSuccess) s.ptr = p;
+  });
+  if (s.err != hipSuccess)
+    return fail(FG8_EHIP, "%s: scratch set-up failed: %s", fn, hipGetErrorString(s.err));
+  *out = s.ptr;
+  return FG8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fg8_status gemm_fp8_blockscaled_noalloc(const uint8_t* a, const float* sa, const uint8_t* b,
+                                        const float* sb, void* d, fg8_out out, int64_t m,
+                                        int64_t n, int64_t k, hipStream_t stream) {
+  const char* fn = "gemm_fp8_blockscaled_noalloc";
+  FG8_CHECK_PTR(a);
+  FG8_CHECK_PTR(sa);
+  FG8_CHECK_PTR(b);
+  FG8_CHECK_PTR(sb);
+  FG8_CHECK_PTR(d);
+  if (out != FG8_OUT_F32 && out != FG8_OUT_BF16) return fail(FG8_EINVAL, "%s: bad out", fn);
+  if (m < 1 || n < 1 || m >= kMaxDim || n >= kMaxDim)
+    return fail(FG8_EINVAL, "%s: bad sizes m=%lld n=%lld", fn, (long long)m, (long long)n);
+  if (fg8_status s = check_k(fn, k)) return s;
+  fg8::GemmProblem p{};
+  p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.d = d;
+  p.out_bf16 = out == FG8_OUT_BF16;
+  p.mode = fg8::kDense; p.M = m; p.N = n; p.K = k; p.groups = 1;
+  const int cus = fg8::device_cu_count();
+  const fg8::TileChoice t = fg8::choose_tiles(p, cus);
+  if (fg8_status st = check_units(p, t, fn)) return st;
+  if (t.splits > 1) {
+    const size_t need = fg8::splitk_workspace_bytes(m, n, k, cus);
+    if (need > (size_t)FG8_NOALLOC_SCRATCH_BYTES)
+      return fail(FG8_EUNSUPPORTED, "%s: m=%lld n=%lld k=%lld needs %zu bytes of split-K scratch, "
+                  "more than the %zu this entry point holds (use gemm_fp8_blockscaled with a "
+                  "workspace)", fn, (long long)m, (long long)n, (long long)k, need,
+                  (size_t)FG8_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (fg8_status st = scratch_ptr(fn, stream, &ws)) return st;
+    p.ws_counters = (int32_t*)ws;
+    p.ws_partial = (float*)((char*)ws + fg8::kSplitKCounterBytes);
   }
   const hipError_t e = fg8::launch_gemm(p, t, stream);
   if (e != hipSuccess) return fail(FG8_EHIP, "%s: launch failed: %s", fn, hipGetErrorString(e));

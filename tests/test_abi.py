@@ -179,3 +179,31 @@ def test_kgrouped_and_transposed_quantize_validation(L):
     assert b"transposed" in L.fg8_last_error()
     assert q(ok, 1, 256, 96, 3, ok, ok, None) == 2           # cols % 64
     assert q(ok, 1, 256, 4, 4, ok, ok, None) == 1            # unknown kind
+
+
+def test_noalloc_scratch_covers_every_split_k_workspace(L):
+    """gemm_fp8_blockscaled_noalloc keeps its split-K scratch in a static
+    array of FG8_NOALLOC_SCRATCH_BYTES per GPU; on a 256-CU part no dense
+    shape needs more (split-K is used only while the tiles fill at most one
+    round, so the partials are bounded by one tile per workgroup slot)."""
+    import re
+    cap = int(eval(re.search(r"#define FG8_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)",
+                             open(HEADER).read()).expand(r"\1 << \2")))
+    assert cap == 16 << 20
+    worst = 0
+    for m in (1, 7, 16, 33, 64, 65, 100, 128, 129, 200, 256, 300, 512, 1024):
+        for n in (1, 64, 130, 256, 520, 1000, 2112, 4096, 7168, 16384, 24576):
+            for k in (128, 512, 1024, 2048, 7168, 16384, 65536):
+                need = L.fg8_gemm_workspace_bytes(m, n, k)
+                worst = max(worst, need)
+                assert need <= cap, (m, n, k, need)
+    assert worst > 4096                       # some shapes do use split-K
+    print(f"largest split-K workspace over the sweep: {worst} bytes")
+
+
+def test_noalloc_validation(L):
+    ok = _fake(0x10000)
+    assert L.gemm_fp8_blockscaled_noalloc(None, ok, ok, ok, ok, 0, 64, 64, 128, None) == 1
+    assert b"a is NULL" in L.fg8_last_error()
+    assert L.gemm_fp8_blockscaled_noalloc(ok, ok, ok, ok, ok, 0, 64, 64, 200, None) == 2
+    assert L.gemm_fp8_blockscaled_noalloc(ok, ok, ok, ok, ok, 7, 64, 64, 128, None) == 1
