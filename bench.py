@@ -62,6 +62,8 @@ def parse(argv=None):
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="", help="comma list of extra names to run (profiling)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock sample (for runs under a profiler)")
     return ap.parse_args(argv)
 
 
@@ -308,12 +310,14 @@ def main(argv=None):
     log(f"headline step {t_step * 1e6:.2f} us (events), {t_wall * 1e6:.2f} us wall, "
         f"{value:.1f} TFLOP/s ({R} rotation copies, cold first step {cold_us:.0f} us)")
     single = timer.singles(step_fns, 200)
-    # the shader clock while the timed graph runs (enqueued several times)
-    with torch.cuda.stream(stream):
-        for _ in range(max(1, 80000 // args.steps)):
-            timed_graph.replay()
-    sclk = read_sclk_mhz()
-    torch.cuda.synchronize()
+    # the shader clock while the timed graph runs (enqueued for about 1.5 s)
+    sclk = None
+    if not args.no_clock:
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, min(4000, int(1.5 / (t_step * args.steps))))):
+                timed_graph.replay()
+        sclk = read_sclk_mhz()
+        torch.cuda.synchronize()
     env["sclk_mhz_under_load"] = sclk
     del timed_graph
 
