@@ -29,6 +29,7 @@ struct GemmProblem {
   const int32_t* valid;         // masked: live rows per group (NULL = all M)
   const int32_t* k_offsets;     // K-grouped: K offset of each group [groups + 1]
   int rotate;                   // 1: start each unit's K walk at a unit-dependent block
+  int stagger;                  // 1: half the waves issue the next stage's loads late (Cfg::LATE)
   int raster;                   // > 0: XCD-blocked grouped raster of the tiles, this many tile rows per group
   // contiguous only: 1 = fused SiLU-gated epilogue that writes the 1x128
   // quantization of h = silu(gate) * up (W1 rows interleaved in 128-row
@@ -57,6 +58,7 @@ struct TileChoice {
   int splits;
   int grid;
   int rotate;
+  int stagger;
   int raster;
 };
 
