@@ -30,12 +30,14 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float4 v) {
   return cvt2_e4m3(v.x, v.y) | (cvt2_e4m3(v.z, v.w) << 16);
 }
 
-// Round-to-nearest-even FP32 -> BF16 bits.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return 0x7FC0;  // NaN
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two FP32 values -> two BF16 values (low half from a) with one
+// v_cvt_pk_bf16_f32: round to nearest even, subnormals kept, NaN stays NaN
+// (pinned against torch's CPU cast by the probe tests).
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
 }
 
 // Maximum over the lanes of one aligned group of `width` lanes (power of two

@@ -77,8 +77,10 @@ struct Cfg {
   // Waves w and w + 4 share a SIMD, and an LDS-DMA instruction holds up its
   // wave until the memory pipeline takes it, so with all waves issuing
   // together both waves of a SIMD stall at once; staggered, one of them is
-  // issuing MFMAs while the other waits.
-  static constexpr int LATE = PIN && !SPREAD ? 1 : -1;
+  // issuing MFMAs while the other waits.  Measured on the MoE W1: after
+  // column tile 0, 1, 2 or 3: 1.84, 1.82, 1.80, 1.82 ms (all at once 2.00).
+  // The K-grouped kernel issues after column tile 1 (kernel: LATE_AT).
+  static constexpr int LATE = PIN && !SPREAD ? 2 : -1;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
   // One stage holds KS K blocks, each laid out as: A tile | B tile | A row
@@ -525,7 +527,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
     // load instruction that waits for room in the memory pipeline holds up
     // the wave while its MFMAs are already running.
     constexpr int POINTS = C::KS * C::TN;
-    static_assert(C::LATE < POINTS, "the late issue point lies inside the K block's column steps");
+    // (the K-grouped kernel's per-column scales leave fewer registers: with
+    // the issue after column tile 2 it spills more and ran 2.6% slower)
+    constexpr int LATE_AT = MODE == kKGrouped && C::LATE >= 0 ? 1 : C::LATE;
+    static_assert(LATE_AT < POINTS, "the late issue point lies inside the K block's column steps");
     for (int si = 0; si < nst; ++si) {
       const int later = min(C::STAGES - 2, nst - 1 - si);   // stages issued after this one
       wait_stages_after<LOADS, C::STAGES - 2>(later);
@@ -533,11 +538,11 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       const int nsi = si + C::STAGES - 1;
       const bool more = nsi < nst;
       const int nstage = nsi % C::STAGES;
-      const bool late = C::LATE >= 0 && p.stagger && wave >= C::WAVES / 2 && wave_live;
+      const bool late = LATE_AT >= 0 && p.stagger && wave >= C::WAVES / 2 && wave_live;
       auto issue_point = [&](int pt) {
         if (C::SPREAD && more)
           issue_range(nsi, nstage, pt * LOADS / POINTS, (pt + 1) * LOADS / POINTS);
-        if (pt == C::LATE && late && more) issue_range(nsi, nstage, 0, LOADS);
+        if (pt == LATE_AT && late && more) issue_range(nsi, nstage, 0, LOADS);
       };
       if (!C::SPREAD || !wave_live) {
         if (more && !late) issue_range(nsi, nstage, 0, LOADS);
@@ -783,8 +788,13 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       constexpr int FIT = C::STAGES * C::STAGE_BYTES / ROW;
       constexpr int CR = FIT >= C::BM ? C::BM : (FIT / C::WM) * C::WM;
       static_assert(CR >= C::WM && C::BM % CR == 0, "output rows must stage in whole wave blocks");
+      // a whole staged block is CR * CHUNKS 16-byte pieces, ITER per thread
+      constexpr bool EVEN = C::THREADS % CHUNKS == 0 && (CR * CHUNKS) % C::THREADS == 0;
+      constexpr int ITER = EVEN ? CR * CHUNKS / C::THREADS : 1;
       const int64_t d_off = MODE == kMasked || MODE == kKGrouped ? (int64_t)w.g * M * N : 0;
       const bool vec = (N * ESZ) % 16 == 0;   // every row starts 16-byte aligned
+      // the unit's tile lies inside the output and its rows fit 32-bit offsets
+      const bool full_cols = vec && w.n0 + C::BN <= N && (int64_t)CR * N * ESZ < (1ll << 31);
 #pragma unroll
       for (int r0 = 0; r0 < C::BM; r0 += CR) {
         if (r0 > 0) __syncthreads();   // the previous rows have left LDS
@@ -792,33 +802,73 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
 #pragma unroll
           for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
-            for (int tn = 0; tn < C::TN; ++tn)
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                uint8_t* q = smem + (wm0 - r0 + tm * 16 + 4 * (lane >> 4) + v) * ROW +
+            for (int tn = 0; tn < C::TN; ++tn) {
+              // lane (i + 16 g) holds rows 4 g .. 4 g + 3 of column i
+              if constexpr (ESZ == 2) {
+                uint8_t* q = smem + (wm0 - r0 + tm * 16 + 4 * (lane >> 4)) * ROW +
                              (wn0 + tn * 16 + (lane & 15)) * ESZ;
-                if constexpr (ESZ == 2)
-                  *reinterpret_cast<uint16_t*>(q) = f32_to_bf16(acc[tm][tn][v]);
-                else
-                  *reinterpret_cast<float*>(q) = acc[tm][tn][v];
+                const uint32_t lo = bf16x2(acc[tm][tn][0], acc[tm][tn][1]);
+                const uint32_t hi = bf16x2(acc[tm][tn][2], acc[tm][tn][3]);
+                *reinterpret_cast<uint16_t*>(q) = (uint16_t)lo;
+                *reinterpret_cast<uint16_t*>(q + ROW) = (uint16_t)(lo >> 16);
+                *reinterpret_cast<uint16_t*>(q + 2 * ROW) = (uint16_t)hi;
+                *reinterpret_cast<uint16_t*>(q + 3 * ROW) = (uint16_t)(hi >> 16);
+              } else {
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                  *reinterpret_cast<float*>(smem + (wm0 - r0 + tm * 16 + 4 * (lane >> 4) + v) * ROW +
+                                            (wn0 + tn * 16 + (lane & 15)) * ESZ) = acc[tm][tn][v];
               }
+            }
         }
         __syncthreads();
         const int64_t live = min((int64_t)CR, (int64_t)w.rows - w.m0 - r0);
-        for (int idx = tid; idx < live * CHUNKS; idx += C::THREADS) {
-          const int r = idx / CHUNKS, ch = idx % CHUNKS;
-          const int64_t col = w.n0 + ch * PER;
-          const uint8_t* src = smem + r * ROW + ch * 16;
-          uint8_t* dst =
-              reinterpret_cast<uint8_t*>(p.d) + (d_off + (w.m0 + r0 + r) * N + col) * ESZ;
-          if (vec && col + PER <= N) {
-            *reinterpret_cast<int4*>(dst) = *reinterpret_cast<const int4*>(src);
-          } else {
-            for (int e = 0; e < PER && col + e < N; ++e) {
-              if constexpr (ESZ == 2)
-                reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
-              else
-                reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src)[e];
+        // rows covered by one pass of all threads over the pieces of a row
+        constexpr int RSTEP = EVEN ? C::THREADS / CHUNKS : 1;
+        if (ESZ == 2 && EVEN && full_cols && live > 0 && live % RSTEP == 0) {
+          // whole passes: all LDS reads first, then the stores (buffer
+          // stores with 32-bit offsets from the block's first row); the
+          // pass guard i * RSTEP < live is uniform
+          uint8_t* dbase = reinterpret_cast<uint8_t*>(p.d) + (d_off + (w.m0 + r0) * N + w.n0) * ESZ;
+          const __amdgpu_buffer_rsrc_t out = buffer_rsrc(dbase, (uint32_t)((int64_t)CR * N * ESZ));
+          // (an opaque copy of tid: the offsets below are computed here, not
+          // hoisted into registers held through the main loop)
+          int t = tid;
+          asm volatile("" : "+v"(t));
+          const int ch = t % CHUNKS, rr = t / CHUNKS;
+          const uint32_t off0 = (uint32_t)((rr * N + ch * PER) * ESZ);
+          const uint32_t rstep_bytes = (uint32_t)(RSTEP * N * ESZ);
+          constexpr int BATCH = ITER < 4 ? ITER : 4;   // pieces in registers at a time
+#pragma unroll
+          for (int i0 = 0; i0 < ITER; i0 += BATCH) {
+            v4i piece[BATCH];
+#pragma unroll
+            for (int i = i0; i < i0 + BATCH; ++i)
+              if (i * RSTEP < live)
+                piece[i - i0] = *reinterpret_cast<const v4i*>(smem + (rr + i * RSTEP) * ROW + ch * 16);
+#pragma unroll
+            for (int i = i0; i < i0 + BATCH; ++i)
+              if (i * RSTEP < live)
+                __builtin_amdgcn_raw_buffer_store_b128(piece[i - i0], out, off0 + i * rstep_bytes,
+                                                       0, 0);
+            asm volatile("" ::: "memory");   // keep the next batch's reads after these stores
+          }
+        } else {
+          for (int idx = tid; idx < live * CHUNKS; idx += C::THREADS) {
+            const int r = idx / CHUNKS, ch = idx % CHUNKS;
+            const int64_t col = w.n0 + ch * PER;
+            const uint8_t* src = smem + r * ROW + ch * 16;
+            uint8_t* dst =
+                reinterpret_cast<uint8_t*>(p.d) + (d_off + (w.m0 + r0 + r) * N + col) * ESZ;
+            if (vec && col + PER <= N) {
+              *reinterpret_cast<int4*>(dst) = *reinterpret_cast<const int4*>(src);
+            } else {
+              for (int e = 0; e < PER && col + e < N; ++e) {
+                if constexpr (ESZ == 2)
+                  reinterpret_cast<uint16_t*>(dst)[e] = reinterpret_cast<const uint16_t*>(src)[e];
+                else
+                  reinterpret_cast<float*>(dst)[e] = reinterpret_cast<const float*>(src)[e];
+              }
             }
           }
         }
@@ -989,7 +1039,7 @@ TileChoice choose_tiles(const GemmProblem& p, int num_cus) {
   t.rotate = 0;
   if (const char* e = getenv("FG8_ROTATE")) t.rotate = atoi(e) != 0;
   // Staggered load issue on the two-stage 256 x 256 tiles: on (W1 of the
-  // MoE workload 2.02 -> 1.87 ms, W2 -3.6%, 4096 x 7168 x 2048 -3.8%).
+  // MoE workload 2.00 -> 1.80 ms, W2 -5%, 4096 x 7168 x 2048 -4%).
   t.stagger = 1;
   if (const char* e = getenv("FG8_STAGGER")) t.stagger = atoi(e) != 0;
   // XCD-blocked tile order, four tile rows per group, for the 256 x 256

@@ -58,6 +58,17 @@ __global__ void k_cvt(const float* x, uint32_t* out, int npairs, int clamp) {
   out[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
 }
 
+// n floats -> n/2 words of two BF16 values (v_cvt_pk_bf16_f32: low half from
+// the first float).
+__global__ void k_cvt_bf16(const float* x, uint32_t* out, int npairs) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= npairs) return;
+  const f2 v = {x[2 * i], x[2 * i + 1]};
+  out[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
+}
+
 __global__ void k_copy(const float4* __restrict__ src, float4* __restrict__ dst, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -99,6 +110,11 @@ int probe_mfma32_acc(const void* a, const void* b, const void* c, void* d, hipSt
 int probe_cvt_fp8(const void* x, void* out, int npairs, int clamp, hipStream_t s) {
   hipLaunchKernelGGL(k_cvt, dim3((npairs + 255) / 256), dim3(256), 0, s, (const float*)x,
                      (uint32_t*)out, npairs, clamp);
+  return (int)hipGetLastError();
+}
+int probe_cvt_bf16(const void* x, void* out, int npairs, hipStream_t s) {
+  hipLaunchKernelGGL(k_cvt_bf16, dim3((npairs + 255) / 256), dim3(256), 0, s, (const float*)x,
+                     (uint32_t*)out, npairs);
   return (int)hipGetLastError();
 }
 int probe_copy(const void* src, void* dst, size_t n_float4, int blocks, hipStream_t s) {

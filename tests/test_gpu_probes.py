@@ -6,6 +6,8 @@
     32-element chunk, and the bias 127;
   * v_cvt_pk_fp8_f32: round-to-nearest-even, saturation and the sign of zero,
     compared with the oracle's encoder on a sweep through every e4m3 midpoint;
+  * v_cvt_pk_bf16_f32 (the BF16 output conversion): round-to-nearest-even
+    on ties, overflow, subnormals and signed zeros, against torch's CPU cast;
   * e4m3 subnormal operands times normal ones are used exactly by the FP8
     MFMA (scaled and unscaled); products of two subnormals are reported;
   * how one MFMA rounds its 128-product sum (informational).
@@ -34,7 +36,8 @@ def env():
         raise RuntimeError("probe library not built: run __graft_entry__.build()")
     lib = ctypes.CDLL(LIB)
     for name in ("probe_mfma16", "probe_mfma32", "probe_mfma16_scaled", "probe_mfma32_scaled",
-                 "probe_mfma16_acc", "probe_mfma32_acc", "probe_cvt_fp8", "probe_copy"):
+                 "probe_mfma16_acc", "probe_mfma32_acc", "probe_cvt_fp8", "probe_cvt_bf16",
+                 "probe_copy"):
         getattr(lib, name).restype = ctypes.c_int
     return torch, lib
 
@@ -216,6 +219,53 @@ def test_cvt_pk_fp8_f32(env, clamp):
         # without a pre-clamp only out-of-range magnitudes may differ
         assert np.all(np.abs(x[bad]) > 448), msg
         print(f"\nunclamped cvt differs on {bad.size} values: {msg}")
+
+
+def _bf16_sweep():
+    g = np.random.default_rng(105)
+    hi = g.integers(0, 1 << 16, 6000, dtype=np.uint32) << 16
+    pts = [hi,                                    # BF16 values themselves
+           hi | 0x8000,                           # exact ties: even and odd neighbours
+           hi | 0x7FFF, hi | 0x8001,              # just below / above the tie
+           g.integers(0, 1 << 32, 20000, dtype=np.uint64).astype(np.uint32),
+           np.array([0x00000001, 0x00008000, 0x00018000, 0x007FFFFF, 0x00800000,  # subnormals
+                     0x7F7F7FFF, 0x7F7F8000, 0x7F7FFFFF,                       # overflow edge
+                     0x7F800000, 0x3F808000, 0x3F818000, 0x00000000], np.uint32)]
+    u = np.concatenate(pts).astype(np.uint32)
+    u = np.concatenate([u, u ^ 0x80000000])       # both signs
+    x = u.view(np.float32)
+    x = x[np.isfinite(x) | np.isinf(x)]           # NaNs are checked on their own
+    if x.size % 2:
+        x = np.append(x, np.float32(1.0))
+    return x
+
+
+def test_cvt_pk_bf16_f32(env):
+    torch, lib = env
+    x = _bf16_sweep()
+    tx = torch.from_numpy(x).cuda()
+    out = torch.zeros(x.size // 2, dtype=torch.int32, device="cuda")
+    rc = lib.probe_cvt_bf16(ctypes.c_void_p(tx.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                            ctypes.c_int(x.size // 2), _stream(torch))
+    assert rc == 0
+    w = out.cpu().numpy().view(np.uint32)
+    got = np.empty(x.size, np.uint16)
+    got[0::2] = w & 0xFFFF
+    got[1::2] = w >> 16
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bad = np.nonzero(got != want)[0]
+    msg = "; ".join(f"{x.view(np.uint32)[i]:#010x}: hw {got[i]:#06x} torch {want[i]:#06x}"
+                    for i in bad[:12])
+    assert bad.size == 0, msg
+    # NaN in, NaN out (exponent all ones, mantissa not zero)
+    nan = np.array([np.nan, -np.nan], np.float32)
+    tn = torch.from_numpy(nan).cuda()
+    o = torch.zeros(1, dtype=torch.int32, device="cuda")
+    assert lib.probe_cvt_bf16(ctypes.c_void_p(tn.data_ptr()), ctypes.c_void_p(o.data_ptr()),
+                              ctypes.c_int(1), _stream(torch)) == 0
+    wn = int(o.cpu().numpy().view(np.uint32)[0])
+    for h in (wn & 0xFFFF, wn >> 16):
+        assert (h & 0x7F80) == 0x7F80 and (h & 0x7F) != 0, hex(h)
 
 
 def _one_product(torch, lib, ca, cb, scaled=False):
