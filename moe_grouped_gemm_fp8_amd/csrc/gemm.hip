@@ -825,7 +825,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
         const int64_t live = min((int64_t)CR, (int64_t)w.rows - w.m0 - r0);
         // rows covered by one pass of all threads over the pieces of a row
         constexpr int RSTEP = EVEN ? C::THREADS / CHUNKS : 1;
-        if (ESZ == 2 && EVEN && full_cols && live > 0 && live % RSTEP == 0) {
+        if (EVEN && full_cols && live > 0 && live % RSTEP == 0) {
           // whole passes: all LDS reads first, then the stores (buffer
           // stores with 32-bit offsets from the block's first row); the
           // pass guard i * RSTEP < live is uniform
