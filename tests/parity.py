@@ -259,7 +259,7 @@ def check_swiglu_quant(q, s, C, S, F, K, where=""):
     dq = e4m3.decode(np.asarray(q, np.uint8))
     h = activation.swiglu_interleaved(C)
 
-    def verdict(T):
+    def outcome(T):
         g, u = activation.gate_up_of(C)
         Tg, Tu = activation.gate_up_of(T)
         E0 = 1.1 * Tg * (np.abs(u) + Tu) + np.abs(activation.silu(g)) * Tu
@@ -282,7 +282,7 @@ def check_swiglu_quant(q, s, C, S, F, K, where=""):
         ok_q = (dq >= lo) & (dq <= hi)
         return ok_s, ok_q
 
-    ok_s, ok_q = verdict(eps_acc(K) * S)
+    ok_s, ok_q = outcome(eps_acc(K) * S)
     # groups (row, 128-column block of h) with a failing scale or code are
     # re-checked with S_trunc of their gate and up elements
     bad_grp = ~ok_s | ~ok_q.reshape(R, H // 128, 128).all(axis=2)
@@ -293,7 +293,7 @@ def check_swiglu_quant(q, s, C, S, F, K, where=""):
         rows = np.repeat(r, 256)
         T = eps_acc(K) * S
         T[rows, cols] += Ft.at(rows * N2 + cols)
-        ok_s, ok_q = verdict(T)
+        ok_s, ok_q = outcome(T)
     assert ok_s.all(), f"{where}: {np.count_nonzero(~ok_s)} scales outside their bounds"
     assert ok_q.all(), f"{where}: {np.count_nonzero(~ok_q)} of {ok_q.size} codes outside their bounds"
     sf = np.repeat(s_gpu, 128, axis=1)
