@@ -519,8 +519,43 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
         if (q >= p0 && q < p1)
           issue_part(kb_of(min(si * C::KS + q / PB, nkb - 1)), stage, q / PB, q % PB);
     };
-    for (int s = 0; s < C::STAGES - 1; ++s)
-      if (s < nst) issue_range(s, s, 0, LOADS);
+    // SAB (masked layout, two-stage 256 x 256 tiles, FP32 block scales):
+    // the A part of a K block (A rows and their scales) and its B part (B
+    // rows and the B-block scale) are issued separately.  A wave reads its
+    // A fragments and the scales into registers when it starts a K block,
+    // so once every wave is past column tile MID_AT the block's A region is
+    // dead: a barrier there lets the A part of the K block two ahead go
+    // into it, giving A two blocks of compute to land while only the B part
+    // of the next block must land within one.  The masked GEMM streams each
+    // expert's B from HBM once and gains (0.119 -> 0.114 ms); on the other
+    // layouts the extra barrier cost more than the slack gained.
+    constexpr bool SAB = C::PIN && C::STAGES == 2 && C::KS == 1 && !MX && MODE == kMasked;
+    constexpr int NA = C::A_LOADS + 1;   // loads of an A part, per wave
+    constexpr int MID_AT = 2, B_LATE_AT = 1, A_LATE_AT = 5;
+    static_assert(!SAB || (MID_AT < C::TN && A_LATE_AT < C::TN && B_LATE_AT < MID_AT &&
+                           MID_AT < A_LATE_AT), "issue points inside the column steps, B before A");
+    auto issue_A = [&](int si, int stage) {
+      const int kb = kb_of(min(si, nkb - 1));
+#pragma unroll
+      for (int r = 0; r < C::A_LOADS; ++r) issue_part(kb, stage, 0, r);
+      issue_part(kb, stage, 0, C::A_LOADS + C::B_LOADS);
+    };
+    auto issue_B = [&](int si, int stage) {
+      const int kb = kb_of(min(si, nkb - 1));
+#pragma unroll
+      for (int r = C::A_LOADS; r < C::A_LOADS + C::B_LOADS; ++r) issue_part(kb, stage, 0, r);
+      issue_part(kb, stage, 0, C::A_LOADS + C::B_LOADS + 1);
+    };
+    if constexpr (SAB) {
+      if (nst > 0) {
+        issue_A(0, 0);
+        issue_B(0, 0);
+      }
+      if (nst > 1) issue_A(1, 1);
+    } else {
+      for (int s = 0; s < C::STAGES - 1; ++s)
+        if (s < nst) issue_range(s, s, 0, LOADS);
+    }
 
     // ---- main loop.  The loads of stage si + STAGES - 1 are spread over the
     // compute of stage si (after the MFMAs of each column tile), so that a
@@ -532,19 +567,45 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
     constexpr int LATE_AT = MODE == kKGrouped && C::LATE >= 0 ? 1 : C::LATE;
     static_assert(LATE_AT < POINTS, "the late issue point lies inside the K block's column steps");
     for (int si = 0; si < nst; ++si) {
-      const int later = min(C::STAGES - 2, nst - 1 - si);   // stages issued after this one
-      wait_stages_after<LOADS, C::STAGES - 2>(later);
+      if constexpr (SAB) {
+        // stage si's A part (issued two blocks ago) and B part are complete;
+        // the A part of block si + 1, issued after them, may stay in flight
+        if (si + 1 < nst) wait_vmcnt<NA>();
+        else wait_vmcnt<0>();
+      } else {
+        const int later = min(C::STAGES - 2, nst - 1 - si);   // stages issued after this one
+        wait_stages_after<LOADS, C::STAGES - 2>(later);
+      }
       __syncthreads();
       const int nsi = si + C::STAGES - 1;
       const bool more = nsi < nst;
       const int nstage = nsi % C::STAGES;
       const bool late = LATE_AT >= 0 && p.stagger && wave >= C::WAVES / 2 && wave_live;
+      const bool moreA = si + 2 < nst;   // SAB: the A part two blocks ahead
       auto issue_point = [&](int pt) {
-        if (C::SPREAD && more)
-          issue_range(nsi, nstage, pt * LOADS / POINTS, (pt + 1) * LOADS / POINTS);
-        if (pt == LATE_AT && late && more) issue_range(nsi, nstage, 0, LOADS);
+        if constexpr (SAB) {
+          // B part of block si + 1 (late waves), the barrier after which this
+          // block's A region is free, the A part of block si + 2
+          if (pt == B_LATE_AT && late && more) issue_B(nsi, nstage);
+          if (pt == MID_AT) {
+            __syncthreads();
+            if (!late && moreA) issue_A(si + 2, si & 1);
+          }
+          if (pt == A_LATE_AT && late && moreA) issue_A(si + 2, si & 1);
+        } else {
+          if (C::SPREAD && more)
+            issue_range(nsi, nstage, pt * LOADS / POINTS, (pt + 1) * LOADS / POINTS);
+          if (pt == LATE_AT && late && more) issue_range(nsi, nstage, 0, LOADS);
+        }
       };
-      if (!C::SPREAD || !wave_live) {
+      if constexpr (SAB) {
+        if (more && !late) issue_B(nsi, nstage);
+        if (!wave_live) {   // (every wave meets the middle barrier)
+          __syncthreads();
+          if (moreA) issue_A(si + 2, si & 1);
+          continue;
+        }
+      } else if (!C::SPREAD || !wave_live) {
         if (more && !late) issue_range(nsi, nstage, 0, LOADS);
         if (!wave_live) continue;
       }
