@@ -238,8 +238,8 @@ def _poison(qa, sa_or_e, valid, scale_axis_rows):
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_masked_small(dev, out_dtype):
-    E, cap, N, K = 7, 96, 200, 512
+def test_masked_small(dev, out_dtype, K=512):
+    E, cap, N = 7, 96, 200
     valid = [0, 96, 1, 37, 64, 95, 50]
     v, a, b = _masked_inputs(E, cap, N, K, valid=valid)
     qa, sa = scaling.quantize_1x128(a)

@@ -68,6 +68,27 @@ def test_mx_masked_scale_groups(dev, tiles256, K):
     G.test_mx_masked_small(dev, torch.float32, K=K)
 
 
+@pytest.mark.parametrize("K", [128, 256, 384, 640])
+def test_masked_few_k_blocks(dev, tiles256, K):
+    """The masked FP32-scaled tiles issue the A part of a stage two K blocks
+    ahead: one, two, three and five K blocks cover the pipeline's start and
+    end (nothing ahead, one block ahead, an odd tail)."""
+    G.test_masked_small(dev, torch.bfloat16, K=K)
+
+
+@pytest.mark.parametrize("knob", [("FG8_STAGGER", "0"), ("FG8_ROTATE", "1")])
+def test_tuning_knobs(dev, tiles256, monkeypatch, knob):
+    """The issue-order and K-walk knobs select other code paths in the same
+    kernels (every wave issuing a stage at once; each unit starting its K
+    walk at a unit-dependent block): same oracle checks."""
+    monkeypatch.setenv(*knob)
+    D.test_dense_parity(dev, "prefill_b", 300, 1000, 1024, torch.bfloat16)
+    G.test_contiguous_small(dev, (700, 1024, 200, 9, 3), torch.bfloat16)
+    G.test_masked_small(dev, torch.float32)
+    G.test_mx_masked_small(dev, torch.float32, K=1152)
+    S.test_swiglu_small(dev, (300, 512, 512, 6, 2))
+
+
 def test_masked_clamped_counts(dev, tiles256):
     G.test_masked_counts_are_clamped(dev)
 
