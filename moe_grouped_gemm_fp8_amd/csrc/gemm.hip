@@ -557,10 +557,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
         if (s < nst) issue_range(s, s, 0, LOADS);
     }
 
-    // ---- main loop.  The loads of stage si + STAGES - 1 are spread over the
-    // compute of stage si (after the MFMAs of each column tile), so that a
-    // load instruction that waits for room in the memory pipeline holds up
-    // the wave while its MFMAs are already running.
+    // ---- main loop.  Where the loads of stage si + STAGES - 1 are issued
+    // during the compute of stage si: on the three-stage SPREAD tiles, a
+    // share after the MFMAs of each column tile, so that a load instruction
+    // that waits for room in the memory pipeline holds up the wave while its
+    // MFMAs are already running; on the two-stage 256 x 256 tiles, right
+    // after the barrier by the first half of the waves and after column tile
+    // LATE_AT by the second half (Cfg::LATE), or split into A and B parts
+    // (SAB above); elsewhere all at once after the barrier.
     constexpr int POINTS = C::KS * C::TN;
     // (the K-grouped kernel's per-column scales leave fewer registers: with
     // the issue after column tile 2 it spills more and ran 2.6% slower)
