@@ -24,6 +24,9 @@ FLAGS = [
     # MFMA results in VGPRs: the promotion FMAs read them directly instead of
     # copying each one out of AGPRs first.
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # Kernel arguments that fit in 16 SGPRs are preloaded by the hardware at
+    # wave launch instead of loaded by the kernel's first instructions.
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
 ]
 
