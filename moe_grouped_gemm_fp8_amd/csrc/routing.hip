@@ -243,6 +243,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(
 // scale 1).  Items [0, tokens) are token rows, one wave each, read once and
 // quantized once with 16-byte loads; items tokens + b clear the padding rows
 // of 128-row block b.
+//
+// A wave issues all loads of a chunk of its row (up to kChunkLoads 16-byte
+// loads per lane) and the token's destination rows (lane j holds the j-th)
+// before any store, quantizes the chunk into registers, and only then writes
+// it to every destination row, reading each row index from a lane with
+// readlane.  The vector-memory counter counts stores as well as loads and
+// completes in order, so a load issued after stores can only be waited for
+// by waiting for those stores too: no load sits between the stores of a
+// chunk.
+constexpr int kChunkLoads = 16;   // 8192 BF16 or 4096 FP32 columns per chunk
+
 template <class T>
 __global__ __launch_bounds__(256) void route_scatter_quant_kernel(
     const T* __restrict__ x, const int32_t* __restrict__ token_row,
@@ -251,7 +262,7 @@ __global__ __launch_bounds__(256) void route_scatter_quant_kernel(
   constexpr int EPL = RowVec<T>::kElems;   // elements per lane per load
   constexpr int LPG = kGroup / EPL;        // lanes per 128-column group
   constexpr int SPAN = 64 * EPL;           // columns per wave load
-  constexpr int U = 4;                     // loads in flight per lane
+  constexpr int U = kChunkLoads;
   const int lane = threadIdx.x & 63;
   const int64_t items = tokens + m_cap / kGroup;
   for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < items;
@@ -259,37 +270,51 @@ __global__ __launch_bounds__(256) void route_scatter_quant_kernel(
     if (it < tokens) {
       const T* xr = x + it * hidden;
       const int32_t* rows = token_row + it * topk;
+      int rv = 0;   // destination row j0 + lane of the token
       for (int64_t c0 = 0; c0 < hidden; c0 += U * SPAN) {
+        if (c0 == 0 || topk > 64) rv = lane < topk ? rows[lane] : -1;
         uint4 raw[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int64_t col = c0 + u * SPAN + lane * EPL;
           raw[u] = col < hidden ? *reinterpret_cast<const uint4*>(xr + col) : make_uint4(0, 0, 0, 0);
         }
+        uint32_t code[U][EPL / 4];
+        float sc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const int64_t col = c0 + u * SPAN + lane * EPL;
           float f[EPL];
           RowVec<T>::widen(raw[u], f);
           float m = 0.f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) m = fmaxf(m, fabsf(f[e]));
           const float amax = group_max<LPG>(m);
-          const float sc = amax == 0.f ? 1.f : amax / kE4m3Max;
-          uint32_t code[EPL / 4];
+          sc[u] = amax == 0.f ? 1.f : amax / kE4m3Max;
 #pragma unroll
           for (int e = 0; e < EPL / 4; ++e)
-            code[e] = pack4_e4m3(make_float4(f[4 * e] / sc, f[4 * e + 1] / sc, f[4 * e + 2] / sc,
-                                             f[4 * e + 3] / sc));
-          if (col < hidden) {
-            for (int j = 0; j < topk; ++j) {
-              const int64_t r = rows[j];
-              if (r < 0) continue;
-              if constexpr (EPL == 4)
-                *reinterpret_cast<uint32_t*>(q + r * hidden + col) = code[0];
-              else
-                *reinterpret_cast<uint2*>(q + r * hidden + col) = make_uint2(code[0], code[1]);
-              if ((lane & (LPG - 1)) == 0) sa[(col / kGroup) * m_cap + r] = sc;
+            code[u][e] = pack4_e4m3(make_float4(f[4 * e] / sc[u], f[4 * e + 1] / sc[u],
+                                                f[4 * e + 2] / sc[u], f[4 * e + 3] / sc[u]));
+        }
+        for (int j0 = 0; j0 < topk; j0 += 64) {
+          // more than 64 destinations: the next 64 row indices (this load,
+          // like the reload of the first 64 for a later chunk, waits for the
+          // stores before it; top-k routings stay far below 64)
+          if (j0 > 0) rv = j0 + lane < topk ? rows[j0 + lane] : -1;
+          const int nj = topk - j0 < 64 ? topk - j0 : 64;
+          for (int j = 0; j < nj; ++j) {
+            const int64_t r = __builtin_amdgcn_readlane(rv, j);
+            if (r < 0) continue;
+            uint8_t* qr = q + r * hidden;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              const int64_t col = c0 + u * SPAN + lane * EPL;
+              if (col < hidden) {
+                if constexpr (EPL == 4)
+                  *reinterpret_cast<uint32_t*>(qr + col) = code[u][0];
+                else
+                  *reinterpret_cast<uint2*>(qr + col) = make_uint2(code[u][0], code[u][1]);
+                if ((lane & (LPG - 1)) == 0) sa[(col / kGroup) * m_cap + r] = sc[u];
+              }
             }
           }
         }

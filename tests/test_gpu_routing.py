@@ -75,6 +75,10 @@ EDGE = {
     "spare_capacity": (333, 128, 3, 4, 512, "uniform"),
     "max_experts": (300, 128, 8, 1024, 0, "uniform"),
     "topk_above_experts": (129, 128, 6, 3, 0, "uniform"),
+    # more than 64 destinations per token and rows longer than one load chunk
+    # of the scatter kernel (8192 BF16 / 4096 FP32 columns): its row-index
+    # reloads between chunks and between groups of 64 destinations
+    "topk_80_long_rows": (40, 8576, 80, 5, 0, "uniform"),
 }
 
 
