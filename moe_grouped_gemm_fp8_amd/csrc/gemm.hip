@@ -965,7 +965,7 @@ using CfgS128k2 = Cfg<64, 128, 1, 4, 3, 1, 2>; // 64 x 32
 using CfgM32k2 = Cfg<128, 32, 4, 1, 3, 1, 2>;  // 32 x 32
 using CfgS32x2k2 = Cfg<64, 32, 2, 2, 3, 2, 2>; // 32 x 16, two workgroups per CU
 using CfgHuge8 = Cfg<256, 256, 4, 2, 2, 1, 1>;  // 64 x 128, two waves per SIMD, loads at once
-using CfgS96 = Cfg<64, 96, 2, 2, 3, 1, 2, true>; // 32 x 48, B-block scales per column tile
+using CfgS96 = Cfg<64, 96, 2, 2, 4, 1, 1>;     // 32 x 48, B-block scales per column tile
 
 struct CfgInfo {
   int bm, bn, occ;
