@@ -176,13 +176,16 @@ def test_abi_errors_do_not_launch(dev):
     ("skinny_a", 64, 2112, 7168),    # 48-column wave tiles straddle 128-column B blocks
     ("tiny", 17, 130, 256),          # ragged N, one partial B block
     ("prefill_b", 300, 1000, 1024),  # several tiles in M, split-K
-    ("skinny_a", 64, 2112, 1152),    # 9 K blocks: the last stage holds one
+    ("skinny_a", 64, 2112, 1152),    # 9 K blocks
     ("tiny", 17, 130, 640),          # 5 K blocks, ragged M and N
+    ("tiny", 33, 200, 128),          # one K block: fewer than the prologue's three stages
+    ("skinny_b", 64, 1000, 384),     # three K blocks: exactly the prologue
 ])
 def test_dense_64x96_tiles(dev, monkeypatch, name, M, N, K):
     """The 64 x 96 configuration (index 18 of the compiled list, forced by the
     tuning hook): each wave keeps the scales of both 128-column B blocks its
-    columns can touch and applies them per 16-column tile; two K blocks per
-    stage, so an odd number of K blocks leaves the last stage half used."""
+    columns can touch and applies them per 16-column tile; four stages of one
+    K block, so units with fewer K blocks than the prologue's three stages,
+    and split-K units, are covered."""
     monkeypatch.setenv("FG8_TILE_OVERRIDE", "18")
     test_dense_parity(dev, name, M, N, K, torch.bfloat16)
