@@ -58,8 +58,15 @@ __global__ __launch_bounds__(64 * WPB) void quant_1x128_kernel(const T* __restri
   const int lane = threadIdx.x & 63;
   const int64_t nseg = (cols + seg_cols - 1) / seg_cols;
   // waves walk the items independently (there is no barrier in this kernel)
-  for (int64_t it = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6); it < items;
-       it += (int64_t)gridDim.x * WPB) {
+  // Workgroup b runs on XCD b % 8; on the large launches, numbering the
+  // items so that each XCD takes a contiguous run of rows keeps the scale
+  // lines (32 rows of one K block) that neighbouring rows share in one XCD's
+  // L2 (69,632 x 7168: 0.489 -> 0.480 ms; the one-wave launches of a few
+  // rows keep the plain order, which measured 0.04 us faster there).
+  const int64_t G = gridDim.x;
+  const int64_t b = WPB > 1 && G % 8 == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
+                                          : (int64_t)blockIdx.x;
+  for (int64_t it = b * WPB + (threadIdx.x >> 6); it < items; it += G * WPB) {
     const int64_t grow = it / nseg;               // row over all batches
     const int64_t c_begin = (it - grow * nseg) * seg_cols;
     const int64_t c_end = c_begin + seg_cols < cols ? c_begin + seg_cols : cols;
@@ -125,7 +132,7 @@ static hipError_t launch_q1(const T* x, int64_t rows_all, int64_t rows, int64_t 
                        cols, seg, items);
     return hipGetLastError();
   }
-  const int64_t blocks = (items + 3) / 4;
+  const int64_t blocks = ((items + 3) / 4 + 7) / 8 * 8;   // whole rounds of the eight XCDs
   const unsigned grid = (unsigned)(blocks < (1 << 20) ? blocks : (1 << 20));
   hipLaunchKernelGGL((quant_1x128_kernel<T, 4>), dim3(grid), dim3(256), 0, stream, x, q, s, rows,
                      cols, seg, items);

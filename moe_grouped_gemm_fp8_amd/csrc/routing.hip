@@ -265,8 +265,14 @@ __global__ __launch_bounds__(256) void route_scatter_quant_kernel(
   constexpr int U = kChunkLoads;
   const int lane = threadIdx.x & 63;
   const int64_t items = tokens + m_cap / kGroup;
-  for (int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); it < items;
-       it += (int64_t)gridDim.x * 4) {
+  // Workgroup b runs on XCD b % 8 (workgroups are dealt to the XCDs in
+  // turn).  Numbering the items so that each XCD takes a contiguous run of
+  // them keeps consecutive tokens, whose destination rows share the lines of
+  // the scale array, on one XCD, so those lines fill up in one L2 instead
+  // of leaving eight of them as partial lines.
+  const int64_t G = gridDim.x;
+  const int64_t b = G % 8 == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  for (int64_t it = b * 4 + (threadIdx.x >> 6); it < items; it += G * 4) {
     if (it < tokens) {
       const T* xr = x + it * hidden;
       const int32_t* rows = token_row + it * topk;
@@ -360,7 +366,7 @@ hipError_t launch_route_quantize(const void* x, bool bf16, int64_t tokens, int64
                      dim3(kRouteThreads), 0, stream, ids, tokens, topk, per, num_experts, counts,
                      offsets, split_counts, row_token, token_row, m_cap);
   const int64_t items = tokens + m_cap / kGroup;
-  const int64_t blocks = (items + 3) / 4;
+  const int64_t blocks = ((items + 3) / 4 + 7) / 8 * 8;   // whole rounds of the eight XCDs
   const unsigned grid = (unsigned)(blocks < (1 << 20) ? blocks : (1 << 20));
   if (bf16)
     hipLaunchKernelGGL(route_scatter_quant_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
