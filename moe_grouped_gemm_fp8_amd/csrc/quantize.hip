@@ -125,7 +125,8 @@ static hipError_t launch_q1(const T* x, int64_t rows_all, int64_t rows, int64_t 
   const int64_t seg = q1_seg_cols(rows_all, cols, RowVec<T>::kElems);
   const int64_t items = rows_all * ((cols + seg - 1) / seg);
   // Few items (decode-sized activations): one wave per workgroup, which
-  // measured 3.59 against 3.79 us on 64 x 1536 (the same on 64 x 7168).
+  // measured 3.68 against 3.85 us per launch on 64 x 1536 (64 x 7168
+  // unchanged).
   if (items < 4096) {
     const unsigned grid = (unsigned)items;
     hipLaunchKernelGGL((quant_1x128_kernel<T, 1>), dim3(grid), dim3(64), 0, stream, x, q, s, rows,
