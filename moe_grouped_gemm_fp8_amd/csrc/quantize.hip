@@ -49,40 +49,48 @@ constexpr int kQUnroll = 8;
 template <class T, int WPB>
 __global__ __launch_bounds__(64 * WPB) void quant_1x128_kernel(const T* __restrict__ x,
                                                           uint8_t* __restrict__ q,
-                                                          float* __restrict__ s, int64_t rows,
+                                                          float* __restrict__ s, uint32_t rows,
                                                           int64_t cols, int64_t seg_cols,
-                                                          int64_t items) {
+                                                          uint32_t nseg, uint32_t items) {
   constexpr int EPL = RowVec<T>::kElems;   // elements per lane per load
   constexpr int LPG = kGroup / EPL;        // lanes per 128-column group
   constexpr int SPAN = 64 * EPL;           // columns per wave load
   const int lane = threadIdx.x & 63;
-  const int64_t nseg = (cols + seg_cols - 1) / seg_cols;
   // waves walk the items independently (there is no barrier in this kernel)
   // Workgroup b runs on XCD b % 8; on the large launches, numbering the
   // items so that each XCD takes a contiguous run of rows keeps the scale
   // lines (32 rows of one K block) that neighbouring rows share in one XCD's
   // L2 (69,632 x 7168: 0.489 -> 0.480 ms; the one-wave launches of a few
   // rows keep the plain order, which measured 0.04 us faster there).
-  const int64_t G = gridDim.x;
-  const int64_t b = WPB > 1 && G % 8 == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
-                                          : (int64_t)blockIdx.x;
-  for (int64_t it = b * WPB + (threadIdx.x >> 6); it < items; it += G * WPB) {
-    const int64_t grow = it / nseg;               // row over all batches
-    const int64_t c_begin = (it - grow * nseg) * seg_cols;
+  // The item decode divides in 32 bits (the host keeps items below 2^31):
+  // GPUs have no integer divider, and the 64-bit quotients it used to take
+  // cost ~1.7 us of a 64-row launch (64 x 7168: 3.82 -> 2.1 us).
+  // One-wave launches have exactly one item per workgroup (grid == items),
+  // so their stride needs no load of the grid size.
+  const uint32_t G = WPB == 1 ? items : gridDim.x;
+  const uint32_t b = WPB > 1 && G % 8 == 0 ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8
+                                           : blockIdx.x;
+  for (uint32_t it = b * WPB + (threadIdx.x >> 6); it < items; it += G * WPB) {
+    const uint32_t grow = it / nseg;              // row over all batches
+    const int64_t c_begin = (int64_t)(it - grow * nseg) * seg_cols;
     const int64_t c_end = c_begin + seg_cols < cols ? c_begin + seg_cols : cols;
-    const int64_t b = grow / rows, r = grow - b * rows;
-    const T* xr = x + grow * cols;
-    uint8_t* qr = q + grow * cols;
-    float* sb = s + b * (cols / kGroup) * rows + r;
+    const uint32_t b = grow / rows, r = grow - b * rows;
+    const T* xr = x + (int64_t)grow * cols;
+    uint8_t* qr = q + (int64_t)grow * cols;
+    float* sb = s + (int64_t)b * (cols / kGroup) * rows + r;
     for (int64_t c0 = c_begin; c0 < c_end; c0 += kQUnroll * SPAN) {
       uint4 raw[kQUnroll];
 #pragma unroll
       for (int u = 0; u < kQUnroll; ++u) {
+        if (c0 + u * SPAN >= c_end) break;   // past the run (uniform), as below
         const int64_t col = c0 + u * SPAN + lane * EPL;
         raw[u] = col < c_end ? *reinterpret_cast<const uint4*>(xr + col) : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < kQUnroll; ++u) {
+        // a load wholly past the run: so are the rest (a uniform branch; the
+        // amax exchanges of dead loads had cost ~1.4 us of a 64-row launch)
+        if (c0 + u * SPAN >= c_end) break;
         const int64_t col = c0 + u * SPAN + lane * EPL;
         float f[EPL];
         RowVec<T>::widen(raw[u], f);
@@ -123,20 +131,22 @@ template <class T>
 static hipError_t launch_q1(const T* x, int64_t rows_all, int64_t rows, int64_t cols, uint8_t* q,
                             float* s, hipStream_t stream) {
   const int64_t seg = q1_seg_cols(rows_all, cols, RowVec<T>::kElems);
-  const int64_t items = rows_all * ((cols + seg - 1) / seg);
+  const int64_t nseg = (cols + seg - 1) / seg;
+  const int64_t items = rows_all * nseg;
+  if (items >= (int64_t(1) << 31) || rows >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   // Few items (decode-sized activations): one wave per workgroup, which
   // measured 3.68 against 3.85 us per launch on 64 x 1536 (64 x 7168
   // unchanged).
   if (items < 4096) {
     const unsigned grid = (unsigned)items;
-    hipLaunchKernelGGL((quant_1x128_kernel<T, 1>), dim3(grid), dim3(64), 0, stream, x, q, s, rows,
-                       cols, seg, items);
+    hipLaunchKernelGGL((quant_1x128_kernel<T, 1>), dim3(grid), dim3(64), 0, stream, x, q, s,
+                       (uint32_t)rows, cols, seg, (uint32_t)nseg, (uint32_t)items);
     return hipGetLastError();
   }
   const int64_t blocks = ((items + 3) / 4 + 7) / 8 * 8;   // whole rounds of the eight XCDs
   const unsigned grid = (unsigned)(blocks < (1 << 20) ? blocks : (1 << 20));
-  hipLaunchKernelGGL((quant_1x128_kernel<T, 4>), dim3(grid), dim3(256), 0, stream, x, q, s, rows,
-                     cols, seg, items);
+  hipLaunchKernelGGL((quant_1x128_kernel<T, 4>), dim3(grid), dim3(256), 0, stream, x, q, s,
+                     (uint32_t)rows, cols, seg, (uint32_t)nseg, (uint32_t)items);
   return hipGetLastError();
 }
 
