@@ -191,6 +191,10 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
   const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int wm0 = wm * C::WM, wn0 = wn * C::WN;
   const int64_t M = p.M, N = p.N, K = p.K;
+  // The problem struct spans three 64-byte scalar-cache lines; taking one
+  // field of each here issues their fetches together, one round trip to
+  // kernel-argument memory instead of a chain of dependent ones.
+  asm volatile("" ::"s"(p.a), "s"(K), "s"(p.ws_counters));
   const int KB = (int)(K / kGroup);
   const int n_tiles = (int)((N + C::BN - 1) / C::BN);
   const int splits = MODE == kDense ? p.splits : 1;
