@@ -39,6 +39,7 @@ struct GemmProblem {
   float* s_out;
   // split-K (dense only)
   int splits;
+  int grid;                     // workgroups of the launch (set by the launcher)
   float* ws_partial;
   int32_t* ws_counters;
 };

@@ -191,12 +191,12 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
   const int wm = wave % C::WAVES_M, wn = wave / C::WAVES_M;
   const int wm0 = wm * C::WM, wn0 = wn * C::WN;
   const int64_t M = p.M, N = p.N, K = p.K;
-  // The problem struct spans three 64-byte scalar-cache lines; taking one
-  // field of each here issues their fetches together, one round trip to
+  // Taking one field of every 32 bytes of the problem struct here issues
+  // all its scalar-cache fetches together, one round trip to
   // kernel-argument memory instead of a chain of dependent ones.
-  asm volatile("" ::"s"(p.a), "s"(K), "s"(p.ws_counters));
+  asm volatile("" ::"s"(p.a), "s"(p.d), "s"(N), "s"(p.valid), "s"(p.q_out), "s"(p.ws_counters));
   const int KB = (int)(K / kGroup);
-  const int n_tiles = (int)((N + C::BN - 1) / C::BN);
+  const int n_tiles = (int)(((uint32_t)N + C::BN - 1) / C::BN);   // N < 2^31 (C ABI)
   const int splits = MODE == kDense ? p.splits : 1;
   const int64_t nb_blocks = (N + kGroup - 1) / kGroup;
 
@@ -253,13 +253,17 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
   const uint32_t lds0 = lds_addr(smem);
   const uint32_t mxg0 = lds_addr(mx_grp);
 
-  for (int u = blockIdx.x; u < total; u += gridDim.x) {
+  // The grid size comes in the problem struct: reading gridDim loads the
+  // launch's hidden arguments, a scalar-cache miss on the path to each
+  // unit's first loads.
+  const int G = p.grid;
+  for (int u = blockIdx.x; u < total; u += G) {
     // ---- decode the unit
     Unit w;
     if constexpr (MODE == kMasked) {
       // with the XCD-blocked order an XCD runs consecutive tiles, mostly of
       // one expert, so that expert's A rows are fetched into its L2 once
-      const int uu = p.raster > 0 ? xcd_block(u, total, gridDim.x) : u;
+      const int uu = p.raster > 0 ? xcd_block(u, total, G) : u;
       int lo = 0, hi = p.groups - 1;   // last group with prefix <= uu
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -294,7 +298,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       const int t = u - h * pair_units;
       int pr = t / n_tiles, nt = t % n_tiles;
       if (h == 0 && p.raster > 0)
-        grouped_tile(xcd_block(t, pair_units, gridDim.x), (int)((mblocks + 1) / 2), n_tiles,
+        grouped_tile(xcd_block(t, pair_units, G), (int)((mblocks + 1) / 2), n_tiles,
                      p.raster, pr, nt);
       const int64_t b0 = 2 * (int64_t)pr;
       w.n0 = (int64_t)nt * C::BN;
@@ -312,17 +316,22 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       }
       w.kb0 = 0; w.kb1 = KB; w.split = 0; w.tile = u;
     } else {
-      const int t = u / splits;
-      w.split = u % splits;
+      // (32-bit quotients on the wave-uniform unit index: the GPU has no
+      // integer divider, and this decode sits on the path to a unit's
+      // first loads)
+      const int uu = __builtin_amdgcn_readfirstlane(u);
+      const int t = uu / splits;
+      w.split = uu - t * splits;
       w.tile = t;
       int mt = t / n_tiles, nt = t % n_tiles;
-      if (splits == 1 && p.raster > 0)
-        grouped_tile(xcd_block(t, total, gridDim.x), (int)((M + C::BM - 1) / C::BM), n_tiles,
+      // (the XCD-blocked raster is compiled into the 256 x 256 tiles only)
+      if (C::PIN && splits == 1 && p.raster > 0)
+        grouped_tile(xcd_block(t, total, G), (int)((M + C::BM - 1) / C::BM), n_tiles,
                      p.raster, mt, nt);
       w.m0 = (int64_t)mt * C::BM;
       w.n0 = (int64_t)nt * C::BN;
-      w.kb0 = (int)((int64_t)w.split * KB / splits);
-      w.kb1 = (int)((int64_t)(w.split + 1) * KB / splits);
+      w.kb0 = w.split * KB / splits;   // KB < 2^17: the C ABI caps K below 2^24
+      w.kb1 = (w.split + 1) * KB / splits;
       w.rows = (int)M;
       w.g = 0;
       if constexpr (MODE == kContiguous) w.g = p.block_expert[w.m0 / kGroup];
@@ -511,7 +520,9 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
     // tiles that run at the same time and share an operand (the A rows of a
     // skinny GEMM, the A tile of a row of output tiles) then read different
     // K blocks of it instead of all hitting the same L2 lines at once.
-    const int rot = p.rotate && nkb > 0 && !MXG ? uniform(u % nkb) : 0;   // MXG: groups in order
+    // (compiled into the 256 x 256 tiles only: on the decode tiles its
+    // remainder and K-block remapping sat on the path to the first loads)
+    const int rot = C::PIN && p.rotate && nkb > 0 && !MXG ? uniform(u % nkb) : 0;   // MXG: groups in order
     auto kb_of = [&](int j) {
       const int x = j + rot;
       return w.kb0 + (x >= nkb ? x - nkb : x);
@@ -1131,7 +1142,8 @@ size_t splitk_workspace_bytes(int64_t m, int64_t n, int64_t k, int num_cus) {
 }
 
 template <class C, bool MX, int MODE>
-static hipError_t launch(const GemmProblem& p, int grid, hipStream_t s) {
+static hipError_t launch(GemmProblem p, int grid, hipStream_t s) {
+  p.grid = grid;
   hipLaunchKernelGGL((gemm_kernel<C, MX, MODE>), dim3(grid), dim3(C::THREADS), 0, s, p);
   return hipGetLastError();
 }
