@@ -748,9 +748,14 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
 
     // ---- split-K: deterministic last-arriver reduction through the workspace
     if (C::SPLITK && MODE == kDense && splits > 1) {
+      // (an opaque copy of the split count: the per-split tests below are
+      // then formed here instead of being hoisted to the kernel's start,
+      // where they had cost SGPR spills on the path to the first loads)
+      int nsp = splits;
+      asm volatile("" : "+s"(nsp));
       constexpr uint32_t kTileBytes = C::BM * C::BN * 4;
       const __amdgpu_buffer_rsrc_t ws =
-          buffer_rsrc(p.ws_partial + (int64_t)w.tile * splits * (C::BM * C::BN), kTileBytes * splits);
+          buffer_rsrc(p.ws_partial + (int64_t)w.tile * nsp * (C::BM * C::BN), kTileBytes * nsp);
 #pragma unroll
       for (int tm = 0; tm < C::TM; ++tm)
 #pragma unroll
@@ -763,7 +768,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       __syncthreads();          // ... and every other thread's
       if (tid == 0)
         flag = __hip_atomic_fetch_add(p.ws_counters + w.tile, 1, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+                                      __HIP_MEMORY_SCOPE_AGENT) == nsp - 1;
       __syncthreads();
       if (!flag) continue;
       // All partial loads of a batch of output tiles are issued before the
@@ -781,7 +786,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
           for (int s = 0; s < kMaxSplits; ++s) {
             const int t = t0 + b;
             const uint32_t idx = (wave * NT + t) * 64 + lane;
-            if (t < NT && s < splits && s != w.split)
+            if (t < NT && s < nsp && s != w.split)
               part[b][s] = __builtin_bit_cast(
                   v4f, __builtin_amdgcn_raw_buffer_load_b128(ws, s * kTileBytes + idx * 16, 0,
                                                              kCoherent));
@@ -794,7 +799,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
           v4f sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < kMaxSplits; ++s)
-            if (s < splits) sum += s == w.split ? a : part[b][s];
+            if (s < nsp) sum += s == w.split ? a : part[b][s];
           a = sum;
         }
       }
