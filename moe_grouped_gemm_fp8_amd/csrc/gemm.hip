@@ -319,19 +319,24 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
       // (32-bit quotients on the wave-uniform unit index: the GPU has no
       // integer divider, and this decode sits on the path to a unit's
       // first loads)
-      const int uu = __builtin_amdgcn_readfirstlane(u);
-      const int t = uu / splits;
-      w.split = uu - t * splits;
-      w.tile = t;
-      int mt = t / n_tiles, nt = t % n_tiles;
+      const uint32_t uu = __builtin_amdgcn_readfirstlane(u);
+      uint32_t t = uu, sp = 0;
+      if (splits > 1) {
+        t = uu / (uint32_t)splits;
+        sp = uu - t * (uint32_t)splits;
+      }
+      w.split = (int)sp;
+      w.tile = (int)t;
+      int mt = (int)(t / (uint32_t)n_tiles), nt = (int)t - mt * n_tiles;
       // (the XCD-blocked raster is compiled into the 256 x 256 tiles only)
       if (C::PIN && splits == 1 && p.raster > 0)
         grouped_tile(xcd_block(t, total, G), (int)((M + C::BM - 1) / C::BM), n_tiles,
                      p.raster, mt, nt);
       w.m0 = (int64_t)mt * C::BM;
       w.n0 = (int64_t)nt * C::BN;
-      w.kb0 = w.split * KB / splits;   // KB < 2^17: the C ABI caps K below 2^24
-      w.kb1 = (w.split + 1) * KB / splits;
+      // KB < 2^17: the C ABI caps K below 2^24
+      w.kb0 = splits > 1 ? (int)(sp * (uint32_t)KB / (uint32_t)splits) : 0;
+      w.kb1 = splits > 1 ? (int)((sp + 1) * (uint32_t)KB / (uint32_t)splits) : KB;
       w.rows = (int)M;
       w.g = 0;
       if constexpr (MODE == kContiguous) w.g = p.block_expert[w.m0 / kGroup];
@@ -386,30 +391,28 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
     // Per-lane byte offsets of the LDS-DMA sources, relative to the tile's
     // first row (fixed for the unit).  Rows past the live count (or past N)
     // are clamped to the last live row: they are read but never stored.
+    // (tile-relative rows in 32 bits: a tile row times K stays below 2^32,
+    // since K < 2^24; the clamps give the same bits as in 64 bits)
+    const int a_last = (int)(last_row - w.m0), b_last = (int)(N - 1 - w.n0);
+    const uint32_t Ku = (uint32_t)K;
     uint32_t a_off[C::A_LOADS], b_off[C::B_LOADS];
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i) {
       const int r = wave * C::A_ROWS + i * 8 + (lane >> 3);
-      const int64_t gr = w.m0 + r < last_row ? w.m0 + r : last_row;
-      a_off[i] = (uint32_t)((gr - w.m0) * K + (((lane & 7) ^ swz(r)) << 4));
+      a_off[i] = (uint32_t)min(r, a_last) * Ku + (((lane & 7) ^ swz(r)) << 4);
     }
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
       const int r = wave * C::B_ROWS + i * 8 + (lane >> 3);
-      const int64_t gr = w.n0 + r < N - 1 ? w.n0 + r : N - 1;
-      b_off[i] = (uint32_t)((gr - w.n0) * K + (((lane & 7) ^ swz(r)) << 4));
+      b_off[i] = (uint32_t)min(r, b_last) * Ku + (((lane & 7) ^ swz(r)) << 4);
     }
     uint32_t sa_off, sb_off = 0;
     {
-      const int64_t r = w.m0 + wave * C::A_ROWS + lane;
-      const int64_t gr = r < last_row ? r : last_row;
-      sa_off = (uint32_t)((gr - w.m0) * (MX ? K / kMxBlock : 4));
+      sa_off = (uint32_t)min(wave * C::A_ROWS + lane, a_last) * (MX ? Ku / kMxBlock : 4u);
       if constexpr (MX) {
-        const int64_t rb = w.n0 + wave * C::B_ROWS + lane;
-        sb_off = (uint32_t)(((rb < N - 1 ? rb : N - 1) - w.n0) * (K / kMxBlock));
+        sb_off = (uint32_t)min(wave * C::B_ROWS + lane, b_last) * (Ku / kMxBlock);
       } else if constexpr (MODE == kKGrouped) {
-        const int64_t rb = w.n0 + wave * C::B_ROWS + lane;
-        sb_off = (uint32_t)(((rb < N - 1 ? rb : N - 1) - w.n0) * 4);
+        sb_off = (uint32_t)min(wave * C::B_ROWS + lane, b_last) * 4u;
       }
     }
     // MXG: lane l fetches dword (l & 3) of row (l >> 2) of each 16-row slice
