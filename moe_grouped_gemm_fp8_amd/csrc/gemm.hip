@@ -938,7 +938,7 @@ __global__ __launch_bounds__(C::THREADS, C::OCC) void gemm_kernel(GemmProblem p)
             for (int i = i0; i < i0 + BATCH; ++i)
               if (i * RSTEP < live)
                 __builtin_amdgcn_raw_buffer_store_b128(piece[i - i0], out, off0 + i * rstep_bytes,
-                                                       0, 0);
+                                                       0, kStream);
             asm volatile("" ::: "memory");   // keep the next batch's reads after these stores
           }
         } else {

@@ -106,9 +106,9 @@ __global__ __launch_bounds__(64 * WPB) void quant_1x128_kernel(const T* __restri
             code[e] = pack4_e4m3(make_float4(f[4 * e] / sc, f[4 * e + 1] / sc, f[4 * e + 2] / sc,
                                              f[4 * e + 3] / sc));
           if constexpr (EPL == 4)
-            *reinterpret_cast<uint32_t*>(qr + col) = code[0];
+            store_nt(qr + col, code[0]);
           else
-            *reinterpret_cast<uint2*>(qr + col) = make_uint2(code[0], code[1]);
+            store_nt(qr + col, code[0], code[1]);
           if ((lane & (LPG - 1)) == 0) sb[(col / kGroup) * rows] = sc;
         }
       }
@@ -253,6 +253,8 @@ __global__ __launch_bounds__(256) void quant_1x128_t_kernel(const T* __restrict_
   const int cc = t >> 2, piece = t & 3;
   uint8_t* dst = q + b * cols * rows + (c_tile + cc) * rows + rb * kGroup + piece * 32;
   const uint32_t* src = &codes[cc][piece * 8];
+  // (ordinary stores: with the non-temporal hint these 32-byte pieces of
+  // code columns took 8% longer on 67,712 x 7168)
   *reinterpret_cast<uint4*>(dst) = make_uint4(src[0], src[1], src[2], src[3]);
   *reinterpret_cast<uint4*>(dst + 16) = make_uint4(src[4], src[5], src[6], src[7]);
 }
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const T* __restrict_
     const int64_t r = r0 + 8 * i;
     if (r < rows) {
       const float4 y = make_float4(v[i].x / sc, v[i].y / sc, v[i].z / sc, v[i].w / sc);
-      *reinterpret_cast<uint32_t*>(qb + r * cols + col) = pack4_e4m3(y);
+      store_nt(qb + r * cols + col, pack4_e4m3(y));
     }
   }
   if (tid == 0) s[b * rblocks * kblocks + (int64_t)rb * kblocks + cb] = sc;
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const T* __restrict__ x,
     const int E = max(expf - 127 - 8, -127);
     const float inv = __uint_as_float((uint32_t)(127 - E) << 23);   // 2^-E, exact
     const float4 y = make_float4(v.x * inv, v.y * inv, v.z * inv, v.w * inv);
-    *reinterpret_cast<uint32_t*>(q + blk * kMxBlock + sub * 4) = pack4_e4m3(y);
+    store_nt(q + blk * kMxBlock + sub * 4, pack4_e4m3(y));
     if (sub == 0) e[blk] = (uint8_t)(E + 127);
   }
 }

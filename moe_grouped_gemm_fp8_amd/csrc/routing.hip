@@ -316,9 +316,9 @@ __global__ __launch_bounds__(256) void route_scatter_quant_kernel(
               const int64_t col = c0 + u * SPAN + lane * EPL;
               if (col < hidden) {
                 if constexpr (EPL == 4)
-                  *reinterpret_cast<uint32_t*>(qr + col) = code[u][0];
+                  store_nt(qr + col, code[u][0]);
                 else
-                  *reinterpret_cast<uint2*>(qr + col) = make_uint2(code[u][0], code[u][1]);
+                  store_nt(qr + col, code[u][0], code[u][1]);
                 if ((lane & (LPG - 1)) == 0) sa[(col / kGroup) * m_cap + r] = sc[u];
               }
             }
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void route_scatter_quant_kernel(
           pad &= pad - 1;
           const int64_t r = r0 + h * 64 + i;
           for (int64_t c = (int64_t)lane * 16; c < hidden; c += 64 * 16)
-            *reinterpret_cast<uint4*>(q + r * hidden + c) = make_uint4(0, 0, 0, 0);
+            store_nt(q + r * hidden + c, 0u, 0u, 0u, 0u);
           for (int64_t kb = lane; kb < hidden / kGroup; kb += 64) sa[kb * m_cap + r] = 1.f;
         }
       }
