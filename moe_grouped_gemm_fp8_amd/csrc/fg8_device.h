@@ -125,6 +125,14 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                : "v"(voff), "s"(sbase), "s"(lds)
                : "memory", "m0");
 }
+// The same copy with the non-temporal hint, for operand rows that no other
+// workgroup of the launch reads.
+__device__ __forceinline__ void dma16_nt(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
                :
