@@ -36,6 +36,19 @@ __device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* p) {
   return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                      __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
+// The same with the non-temporal hint.
+template <class T>
+__device__ __forceinline__ float4 load4_nt(const T* p) {
+  if constexpr (sizeof(T) == 4) {
+    const uint4 u = load_nt16(p);
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                       __uint_as_float(u.w));
+  } else {
+    const uint2 u = load_nt8(p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+  }
+}
 
 // ---------------------------------------------------------------- 1 x 128
 // Row streaming: a wave owns one run of columns of one row (the whole row when
@@ -84,7 +97,11 @@ __global__ __launch_bounds__(64 * WPB) void quant_1x128_kernel(const T* __restri
       for (int u = 0; u < kQUnroll; ++u) {
         if (c0 + u * SPAN >= c_end) break;   // past the run (uniform), as below
         const int64_t col = c0 + u * SPAN + lane * EPL;
-        raw[u] = col < c_end ? *reinterpret_cast<const uint4*>(xr + col) : make_uint4(0, 0, 0, 0);
+        // (non-temporal loads on the multi-wave launches only: the one-wave
+        // ones are decode-sized, where the hint cost latency)
+        raw[u] = col >= c_end ? make_uint4(0, 0, 0, 0)
+                 : WPB == 1   ? *reinterpret_cast<const uint4*>(xr + col)
+                              : load_nt16(xr + col);
       }
 #pragma unroll
       for (int u = 0; u < kQUnroll; ++u) {
@@ -284,7 +301,7 @@ __global__ __launch_bounds__(256) void quant_128x128_kernel(const T* __restrict_
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int64_t r = r0 + 8 * i;
-    v[i] = r < rows ? load4(xb + r * cols + col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[i] = r < rows ? load4_nt(xb + r * cols + col) : make_float4(0.f, 0.f, 0.f, 0.f);
     m = fmaxf(m, abs_max4(v[i]));
   }
   m = group_max<64>(m);
@@ -314,7 +331,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const T* __restrict__ x,
   const int64_t stride = (int64_t)gridDim.x * 32;   // blocks per grid sweep (256 threads / 8)
   const int sub = threadIdx.x & 7;
   for (int64_t blk = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); blk < nblocks; blk += stride) {
-    const float4 v = load4(x + blk * kMxBlock + sub * 4);
+    const float4 v = load4_nt(x + blk * kMxBlock + sub * 4);
     const float amax = group_max<8>(abs_max4(v));
     // floor(log2 amax) - 8 from the exponent field; subnormal or zero amax
     // lands below -127 and is clamped there with the largest normal result.
