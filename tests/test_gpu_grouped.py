@@ -238,9 +238,8 @@ def _poison(qa, sa_or_e, valid, scale_axis_rows):
 
 
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_masked_small(dev, out_dtype, K=512):
-    E, cap, N = 7, 96, 200
-    valid = [0, 96, 1, 37, 64, 95, 50]
+def test_masked_small(dev, out_dtype, K=512, E=7, cap=96, N=200,
+                      valid=(0, 96, 1, 37, 64, 95, 50)):
     v, a, b = _masked_inputs(E, cap, N, K, valid=valid)
     qa, sa = scaling.quantize_1x128(a)
     qb, sb = scaling.quantize_128x128(b)
@@ -333,9 +332,7 @@ def test_masked_full_size_sampled(dev):
 
 # ------------------------------------------------------------- MXFP8
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_mx_masked_small(dev, out_dtype, K=384):
-    E, cap, N = 5, 80, 160
-    valid = [80, 0, 33, 1, 79]
+def test_mx_masked_small(dev, out_dtype, K=384, E=5, cap=80, N=160, valid=(80, 0, 33, 1, 79)):
     v, a, b = _masked_inputs(E, cap, N, K, workload=42, valid=valid)
     qa, ea = scaling.quantize_mx(a)
     qb, eb = scaling.quantize_mx(b)
@@ -352,6 +349,19 @@ def test_mx_masked_small(dev, out_dtype, K=384):
         if v[e]:
             F = ref_mx(qa[e, :v[e]], ea[e, :v[e]], qb[e], eb[e])[2]
             _check(d[e, :v[e]], C[e, :v[e]], S[e, :v[e]], K, f"mx expert {e}", derived=False, F=F)
+
+
+# capacities above one 256-row tile: each expert spans several tile rows that
+# read the same B rows, so the launch copies B without the non-temporal hint
+# that one-tile-row capacities get; the counts end in the first, a middle and
+# the last tile row
+CAP_ABOVE_TILE = dict(E=3, cap=600, N=200, valid=(600, 257, 130))
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_masked_capacity_above_one_tile(dev, out_dtype):
+    test_masked_small(dev, out_dtype, K=512, **CAP_ABOVE_TILE)
+    test_mx_masked_small(dev, out_dtype, K=384, **CAP_ABOVE_TILE)
 
 
 def test_mx_long_k(dev):

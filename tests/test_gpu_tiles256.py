@@ -59,6 +59,7 @@ def test_contiguous_skipped_blocks(dev, tiles256):
 def test_masked(dev, tiles256, out_dtype):
     G.test_masked_small(dev, out_dtype)
     G.test_mx_masked_small(dev, out_dtype)
+    G.test_masked_capacity_above_one_tile(dev, out_dtype)
 
 
 @pytest.mark.parametrize("K", [640, 1152, 2048])
