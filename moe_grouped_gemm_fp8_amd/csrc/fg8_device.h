@@ -31,7 +31,7 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float4 v) {
 }
 
 // Stores of 4, 8 or 16 code bytes with the non-temporal hint, for the
-// quantize and routing kernels that write whole rows of codes: against
+// quantize and routing kernels that write whole lines of codes: against
 // ordinary stores, 3-5% faster on the large 1x128, 128x128 and MX quantize
 // launches and 22% on the routing scatter (8192x7168 tokens, top-8 of 32).
 // p is aligned to the store's size.
