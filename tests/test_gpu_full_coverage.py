@@ -27,6 +27,7 @@ import moe_grouped_gemm_fp8_amd as fg8
 import inputs
 import moe_cases
 from oracle import e4m3
+from parity import Trunc, check_swiglu_quant
 
 pytestmark = pytest.mark.gpu
 
@@ -199,3 +200,39 @@ def test_kgrouped_full_layout(dev):
         k0, k1 = int(off[e]), int(off[e + 1])
         want = a[:, k0:k1].astype(np.float64) @ b[:, k0:k1].astype(np.float64).T
         _exact(got[e].astype(np.float64), want, f"k-grouped expert {e}")
+
+
+@pytest.mark.timeout(600)
+def test_gated_full_layout(dev):
+    """The W1 GEMM with the SiLU-gated activation and its 1x128 requantize
+    fused, over the full 8192-token top-8 of 32 routing layout, N = 4096
+    (2048 columns of h): with integer operands and unit scales every gate and
+    up value is an exact integer, so the only error left is the activation's
+    FP32 arithmetic (relative 2^-20 in the bounds), and every code and scale
+    of h on every row of every expert's blocks is checked against those
+    bounds."""
+    c = inputs.ContiguousCase()
+    lay = moe_cases.contiguous_layout(inputs.zipf_topk_routing(c.workload, c.tokens, c.experts,
+                                                               c.topk), c.experts)
+    M, N, E = lay.m_total, 4096, c.experts
+    be = lay.block_expert
+    g = np.random.default_rng(707)
+    a, b = _ints(g, (M, K)), _ints(g, (E, N, K))
+    print(f"full coverage gated {M}x{N}x{K}, {E} experts", flush=True)
+    q, s = fg8.grouped_gemm_fp8_contiguous_swiglu(_codes(a), _ones(K // 128, M), _codes(b),
+                                                  _ones(E, N // 128, K // 128),
+                                                  torch.from_numpy(be).cuda())
+    torch.cuda.synchronize()
+    q, s = q.cpu().numpy(), s.cpu().numpy()
+    rows_e = np.repeat(be, 128)
+    moved = 0
+    for e in range(E):
+        r = np.nonzero(rows_e == e)[0]
+        if r.size == 0:
+            continue
+        C = (a[r] @ b[e].T).astype(np.float64)      # exact: integers below 2^12
+        moved += check_swiglu_quant(q[r], s[:, r], C, np.zeros_like(C), Trunc.zeros(C.shape), K,
+                                    f"gated expert {e}")
+        if e % 8 == 7:
+            print(f"  experts 0..{e} checked", flush=True)
+    print(f"gated, every element: {moved} codes off the oracle's own rounding of h", flush=True)
