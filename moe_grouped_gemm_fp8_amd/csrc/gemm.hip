@@ -1153,12 +1153,14 @@ size_t splitk_workspace_bytes(int64_t m, int64_t n, int64_t k, int num_cus) {
 }
 
 // B copies with the non-temporal hint where no other unit of the launch reads
-// the same B rows, or where the decode tiles' two tile rows at most do (64-row
-// tiles, M <= 128): against ordinary copies, 64 x 24576 x 1536 12.4-12.8 ->
-// 11.4-11.6 us, 64 x 2112 x 7168 10.8 -> 10.6 us, 128 x 7168 x 2048 10.7 ->
-// 10.0 us, the masked MXFP8 GEMM with 256-row experts 124 -> 111 us.  Where
-// several tile rows share B (4096 x 7168 x 2048, the contiguous layout) the
-// hint cost 5-7%.
+// the same B rows, or where two tile rows at most do: the dense 64-row tiles,
+// which the tile choice takes for M <= 128 only (the tuning override can
+// force them on larger M, where the hint stays correct but may cost time),
+// and masked experts of one tile row.  Against ordinary copies,
+// 64 x 24576 x 1536 12.4-12.8 -> 11.4-11.6 us, 64 x 2112 x 7168 10.8 ->
+// 10.6 us, 128 x 7168 x 2048 10.7 -> 10.0 us, the masked MXFP8 GEMM with
+// 256-row experts 124 -> 111 us.  Where several tile rows share B
+// (4096 x 7168 x 2048, the contiguous layout) the hint cost 5-7%.
 template <class C, bool MX, int MODE, bool BS = MODE == kDense && C::BM == 64>
 static hipError_t launch(GemmProblem p, int grid, hipStream_t s) {
   p.grid = grid;
