@@ -30,17 +30,12 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float4 v) {
   return cvt2_e4m3(v.x, v.y) | (cvt2_e4m3(v.z, v.w) << 16);
 }
 
-// Stores of 4, 8 or 16 code bytes with the non-temporal hint, for the
-// quantize and routing kernels that write whole lines of codes: against
-// ordinary stores, 3-5% faster on the large 1x128, 128x128 and MX quantize
-// launches and 22% on the routing scatter (8192x7168 tokens, top-8 of 32).
-// p is aligned to the store's size.
 // Loads of 16 or 8 source bytes with the non-temporal hint, for the large
 // quantize launches that read each source element once: 1x128 over
 // 69,632 x 7168 467 -> 451 us, 128x128 813 -> 774 us, MX 875 -> 821 us.
 // The decode-sized 1x128 launch, the routing scatter and the transposed
 // quantize ran slower with them (by 0.45 us, 13% and 1%) and keep ordinary
-// loads.
+// loads.  p is aligned to the load's size.
 __device__ __forceinline__ uint4 load_nt16(const void* p) {
   typedef uint32_t u4 __attribute__((ext_vector_type(4)));
   const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
@@ -51,6 +46,11 @@ __device__ __forceinline__ uint2 load_nt8(const void* p) {
   return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
 }
 
+// Stores of 4, 8 or 16 code bytes with the non-temporal hint, for the
+// quantize and routing kernels that write whole lines of codes: against
+// ordinary stores, 3-5% faster on the large 1x128, 128x128 and MX quantize
+// launches and 22% on the routing scatter (8192x7168 tokens, top-8 of 32).
+// p is aligned to the store's size.
 __device__ __forceinline__ void store_nt(uint8_t* p, uint32_t v) {
   __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
 }
